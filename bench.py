@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify-and-sample step on one MI355X.
+
+One step = one spec_verify call over one batch of the c4 workload
+(B=256 sequences, gamma=8 drafts, V=152064, bf16 target logits and bf16 draft
+probabilities, T=1.0; synthetic inputs, resident in HBM before timing).
+Two input sets generated with different seeds alternate between steps, so
+one step never finds the previous step's rows in the 256 MB last-level cache.
+
+Prints one JSON line: verified sequences/s (value), the dominant kernel's
+roofline (achieved algorithmic GB/s from HIP events recorded on the call's
+stream around each stage, against 8 TB/s), and the fp64 CPU oracle timed on
+this host's cores on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified seqs/sec + achieved HBM GB/s (% of peak) at B=256, gamma=8, V=152064"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_c4.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_rejection_sampling_temp_amd", "csrc", "spec_verify.hip")
+
+
+class HipEvents:
+    """hipEvent_t handles via the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        import torch  # noqa: F401
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(d: dict, min_wall_s: float) -> dict:
+    """The fp64 oracle, untuned, on this host's cores: repeat the whole c4
+    batch until at least ``min_wall_s`` of wall time has passed."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                               d["uniforms"], d["temperature"], n_threads=cores, aux=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_wall_s and reps >= 2:
+            break
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": reps * d["B"] / el, "unit": "seqs/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x the full c4 batch ({d['B']} sequences) in {el:.2f} s wall, "
+                      f"OpenMP over sequences on {cores} threads ({model})"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.0,
+                    help="minimum wall time of the CPU-oracle baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the step has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_rejection_sampling_temp_amd as sv
+    from tests import synth
+    from tests.gpu_util import to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    print("[bench] generating c4 inputs", file=sys.stderr, flush=True)
+    host = [synth.make_inputs("c4", args.seed + i) for i in range(2)]
+    dsets = [to_device(h, dev) for h in host]
+    B, G1, V = host[0]["target_logits"].shape
+    gamma = G1 - 1
+    T = host[0]["temperature"]
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    outs = torch.empty((B, G1), dtype=torch.int32, device=dev)
+    ws = torch.zeros(sv.sv_workspace_bytes(B, gamma, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        x = dsets[i % 2]
+        sv.spec_verify(x["target_logits"], x["draft_probs"], x["draft_tokens"], x["uniforms"], T,
+                       "sample", n_accepted=n_acc, out_tokens=outs, workspace=ws, events=events,
+                       stream=stream)
+
+    # n_b of each input set (deterministic), for the byte accounting
+    n_sets = []
+    for i in range(2):
+        step(i)
+        torch.cuda.synchronize()
+        n_sets.append(n_acc.cpu().numpy().copy())
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    hev = HipEvents()
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(args.steps)]
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    rows_ms = [hev.elapsed_ms(e[0], e[1]) for e in evs]
+    draw_ms = [hev.elapsed_ms(e[1], e[2]) for e in evs]
+    for e in evs:
+        for h in e:
+            hev.destroy(h)
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    seqs_per_s = B * args.steps / elapsed
+    n_per_step = [n_sets[i % 2] for i in range(args.steps)]
+    tokens_per_s = float(sum((n + 1).sum() for n in n_per_step)) / elapsed
+
+    # algorithmic bytes (see the design notes): the row stage must read the
+    # target rows 0..n_b of every sequence; the draw stage reads row n_b of
+    # the target and, when n_b < gamma, row n_b of the draft.
+    s_p = 2
+    s_q = 2
+    rows_bytes = [float(((n + 1) * V * s_p).sum() + B * gamma * (s_p + s_q)) for n in n_sets]
+    draw_bytes = [float((V * s_p + (n < gamma) * V * s_q).sum()) for n in n_sets]
+    mean_rows_ms = float(np.mean(rows_ms))
+    mean_draw_ms = float(np.mean(draw_ms))
+    rows_alg_bytes = float(np.mean([rows_bytes[i % 2] for i in range(args.steps)]))
+    draw_alg_bytes = float(np.mean([draw_bytes[i % 2] for i in range(args.steps)]))
+    achieved = rows_alg_bytes / (mean_rows_ms * 1e-3) / 1e9
+    nominal_bytes = B * G1 * V * s_p + B * gamma * V * s_q
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if tr.get("kernel_source_sha256") == sha:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(host[0], args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": seqs_per_s,
+        "unit": "seqs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "c4: B=256 gamma=8 V=152064, bf16 target logits + bf16 draft probs, "
+                               "T=1.0, z_q~N(0,3^2), z_p=z_q+eps*N(0,1), eps~U(0.2,2.0) per sequence",
+                   "batch": int(B), "gamma": int(gamma), "vocab": int(V), "input_dtype": "bf16"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "k_rows_sample<bf16> (row stage)",
+                     "alg_bytes_per_launch": rows_alg_bytes, "avg_launch_ms": mean_rows_ms},
+        "cpu_baseline": cpu,
+        "tokens_per_s": tokens_per_s,
+        "stages_ms": {"rows": mean_rows_ms, "draw": mean_draw_ms,
+                      "draw_alg_GBps": draw_alg_bytes / (mean_draw_ms * 1e-3) / 1e9},
+        "hbm_nominal": {"bytes_per_step": nominal_bytes,
+                        "GBps": nominal_bytes / (ms_per_step * 1e-3) / 1e9,
+                        "frac": nominal_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "mean_tokens_per_sequence": float(np.mean([(n + 1).mean() for n in n_sets])),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,1173 @@
+// spec_verify.hip -- CDNA4 (gfx950) kernels and C ABI of the batched
+// verify-and-sample step of speculative decoding.
+//
+// Sources (page title, section):
+//   [FI] "Fast Inference from Transformers via Speculative Decoding" (paper
+//        summary page): "Standardized Sampling"; "Speculative Sampling: The
+//        Core Algorithm", Algorithm 1 Phases 3 and 4.
+//   [PB] "Speculative Decoding Paper Breakdown: Lossless Draft-and-Verify
+//        Acceleration for Autoregressive Transformers": section 3, "The
+//        Algorithm at Position i"; "Reference Implementation" (q <= 0 accepts).
+//   [ST] "The exact decoding shortcut that burns compute when guesses miss":
+//        correction_distribution (target row when the residual mass <= 1e-15).
+//
+// Two launches per call, both on the caller's stream:
+//
+//   1. row stage (k_rows_sample / k_rows_greedy).  The grid enumerates
+//      (position k, sequence b, chunk c) with k slowest.  A workgroup streams
+//      one chunk of target row (b, k) with 128-bit loads and reduces it to a
+//      partial (max, sum of exp) -- or (max, first argmax) in greedy mode --
+//      and the last workgroup of a row (arrival counter) merges the row's
+//      partials and takes the acceptance decision for position k, setting
+//      bit k of the sequence's reject mask on a rejection.  A workgroup that
+//      finds an earlier position of its sequence already rejected skips its
+//      chunk: rows past the first rejection are never needed ([FI] Phase 3,
+//      the walk stops at the first rejection), so with position-major launch
+//      order most of them are never read.  The decision at each position is
+//      independent of the others, so skipping changes no result.
+//
+//   2. draw stage (k_draw_sample / k_draw_greedy).  n is the index of the
+//      lowest set bit of the reject mask (gamma if none).  For every sequence
+//      the row n of the target (and of the draft, when n < gamma) is
+//      streamed in chunks; each workgroup computes, in double precision,
+//      e_v = exp((z_v - max)/T) and the chunk sums needed for the residual
+//      mass; the last workgroup of the sequence turns them into the exact
+//      row normaliser, picks the chunk holding the inverse-CDF target and
+//      scans it to find the token.
+//
+// Numerics.  The row stage uses fp32 exp2 with a two-term log2(e)/T and a
+// per-chunk correction of the rounded shift, and accumulates in fp64; the
+// acceptance threshold is formed in fp64.  The draw stage works entirely in
+// fp64 (e_v, normaliser, residual, prefix sums), so its token boundaries
+// agree with an fp64 evaluation to rounding level.
+//
+// Workspace: reject masks and arrival counters, then scratch for partials
+// and per-row statistics.  It must be all zero before a call, and each
+// consumer clears what it read, so a finished call leaves all of it zero
+// again -- whatever shape the next call has.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "spec_verify.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr uint64_t kInvalidBit = 1ull << 63;
+constexpr double kResidEps = 1e-15;  // [ST] correction_distribution
+constexpr double kLog2e = 1.4426950408889634073599246810018921;
+
+// Elements per thread of one row-stage chunk (a chunk is 32 KiB of input).
+constexpr int kEptBf16 = 64;
+constexpr int kEptFp32 = 32;
+constexpr int kChunkBf16 = kEptBf16 * kThreads;  // 16384 elements
+constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
+// Elements per thread of one draw-stage chunk (a chunk is 4096 elements).
+constexpr int kEpt2 = 16;
+constexpr int kChunk2 = kEpt2 * kThreads;
+
+// Per-row statistics written by the row stage, read by the draw stage.
+struct RowStat {
+    float m;       // row max of the raw logits
+    int32_t amax;  // greedy: first index attaining m
+    double S;      // sum_v exp((z_v - m)/T)
+    double P;      // p_k(x_k)
+    double Q;      // q_k(x_k)
+};
+static_assert(sizeof(RowStat) == 32, "RowStat layout");
+
+// Per-chunk partial of the draw stage.
+struct DrawPart {
+    double E;      // sum of e_v over the chunk
+    double EA;     // sum of e_v over {v : p_v > q_v} (residual support)
+    double QA;     // sum of q_v over the same set
+    int32_t lastA; // largest index in the residual support, -1 if none
+    int32_t lastE; // largest index with e_v > 0, -1 if none
+};
+static_assert(sizeof(DrawPart) == 32, "DrawPart layout");
+
+struct Layout {
+    size_t mask_off, cnt1_off, cnt2_off, control_bytes;
+    size_t part1_off, stats_off, part2_off, total;
+    int nch1_max, nch2_max;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout make_layout(int B, int gamma, int V)
+{
+    Layout L;
+    const size_t rows = (size_t)B * (size_t)(gamma + 1);
+    L.nch1_max = (V + kChunkFp32 - 1) / kChunkFp32;
+    L.nch2_max = (V + kChunk2 - 1) / kChunk2;
+    size_t off = 0;
+    L.mask_off = off;  off = align256(off + sizeof(uint64_t) * (size_t)B);
+    L.cnt1_off = off;  off = align256(off + sizeof(uint32_t) * rows);
+    L.cnt2_off = off;  off = align256(off + sizeof(uint32_t) * (size_t)B);
+    L.control_bytes = off;
+    L.part1_off = off; off = align256(off + 2 * sizeof(uint64_t) * rows * (size_t)L.nch1_max);
+    L.stats_off = off; off = align256(off + sizeof(RowStat) * rows);
+    L.part2_off = off; off = align256(off + sizeof(DrawPart) * (size_t)B * (size_t)L.nch2_max);
+    L.total = off;
+    return L;
+}
+
+// ------------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p)
+{
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publishes a block's partial result for the last block of its row or
+// sequence.  Each word goes out with a device-scope atomic exchange, and the
+// exchanged-out old values feed the operand of the caller's arrival-counter
+// increment, so every exchange has completed device-wide before the count
+// that reveals it can be observed.  The last block reads the words back with
+// device-scope atomic loads.  (A release/acquire pair at agent scope orders
+// the same thing but writes back the whole L2 on every block, about ten times
+// the cost of the streaming work itself.)  `zero` is a kernel argument that
+// is always 0 and opaque to the compiler; the result is always 0.
+template <int N>
+__device__ __forceinline__ uint32_t publish(uint64_t* slot, const uint64_t (&w)[N], uint32_t zero)
+{
+    uint64_t dep = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        dep ^= __hip_atomic_exchange(slot + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)(dep ^ (dep >> 32)) & zero;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* base, int64_t idx)
+{
+    if constexpr (DT == SV_FP32) {
+        return static_cast<const float*>(base)[idx];
+    } else {
+        return __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[idx]) << 16);
+    }
+}
+
+__device__ __forceinline__ float load_one_rt(const void* base, int dt, int64_t idx)
+{
+    return dt == SV_FP32 ? load_one<SV_FP32>(base, idx) : load_one<SV_BF16>(base, idx);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_min_i(int v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// Block reductions over kThreads threads; every thread gets the result.
+// `sm` must hold kWaves entries and is free again on return.
+__device__ float block_max(float v, float* sm)
+{
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, sm[w]);
+    __syncthreads();
+    return r;
+}
+__device__ double block_sum(double v, double* sm)
+{
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = sm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r += sm[w];
+    __syncthreads();
+    return r;
+}
+__device__ int block_max_i(int v, int* sm)
+{
+    v = wave_max_i(v);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = sm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = max(r, sm[w]);
+    __syncthreads();
+    return r;
+}
+__device__ int block_min_i(int v, int* sm)
+{
+    v = wave_min_i(v);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = sm[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = min(r, sm[w]);
+    __syncthreads();
+    return r;
+}
+
+// Exclusive prefix sum over the block (thread order); also returns the total.
+__device__ double block_exclusive_scan(double v, double* sm, double* total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        double t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) sm[wid] = incl;
+    __syncthreads();
+    double base = 0.0, tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wid) base += sm[w];
+        tot += sm[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+// Argmax pairs: larger value wins, ties go to the lower index.
+__device__ __forceinline__ void amax_merge(float& v, int& i, float v2, int i2)
+{
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ void block_amax(float& v, int& i, float* smf, int* smi)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float v2 = __shfl_xor(v, o, 64);
+        int i2 = __shfl_xor(i, o, 64);
+        amax_merge(v, i, v2, i2);
+    }
+    if ((threadIdx.x & 63) == 0) { smf[threadIdx.x >> 6] = v; smi[threadIdx.x >> 6] = i; }
+    __syncthreads();
+    v = smf[0]; i = smi[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) amax_merge(v, i, smf[w], smi[w]);
+    __syncthreads();
+}
+
+// Loads this thread's share of one row-stage chunk into registers.  Vector
+// path: 128-bit loads, consecutive threads on consecutive 16-byte pieces
+// (requires a 16-byte aligned row start and V a multiple of the vector
+// width); all loads are issued before any value is used.  Scalar path: one
+// element per load, consecutive threads on consecutive elements.  Elements
+// past V read as -inf; a chunk that ends past V clamps its addresses to the
+// row instead of branching per load.  Element e of x sits at index:
+//   vector: v0 + (j * kThreads + tid) * W + (e % W), j = e / W
+//   scalar: v0 + e * kThreads + tid
+template <int DT, bool VEC, int EPT, bool FULL>
+__device__ __forceinline__ void load_chunk_impl(const void* rowp, int v0, int V, float (&x)[EPT])
+{
+    const int tid = threadIdx.x;
+    if constexpr (VEC) {
+        constexpr int W = DT == SV_BF16 ? 8 : 4;
+        constexpr int NV = EPT / W;
+        constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
+        uint4 raw[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            int idx = v0 + (j * kThreads + tid) * W;
+            if constexpr (!FULL) idx = min(idx, V - W);
+            raw[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(rowp) + (size_t)idx * ES);
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            uint4 w = raw[j];
+            if constexpr (!FULL) {
+                if (v0 + (j * kThreads + tid) * W >= V) {
+                    const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+                    w = make_uint4(ninf, ninf, ninf, ninf);
+                }
+            }
+            if constexpr (DT == SV_BF16) {
+                x[j * 8 + 0] = bf16_lo(w.x); x[j * 8 + 1] = bf16_hi(w.x);
+                x[j * 8 + 2] = bf16_lo(w.y); x[j * 8 + 3] = bf16_hi(w.y);
+                x[j * 8 + 4] = bf16_lo(w.z); x[j * 8 + 5] = bf16_hi(w.z);
+                x[j * 8 + 6] = bf16_lo(w.w); x[j * 8 + 7] = bf16_hi(w.w);
+            } else {
+                x[j * 4 + 0] = __uint_as_float(w.x); x[j * 4 + 1] = __uint_as_float(w.y);
+                x[j * 4 + 2] = __uint_as_float(w.z); x[j * 4 + 3] = __uint_as_float(w.w);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = v0 + e * kThreads + tid;
+            if constexpr (FULL) {
+                x[e] = load_one<DT>(rowp, idx);
+            } else {
+                const float z = load_one<DT>(rowp, min(idx, V - 1));
+                x[e] = idx < V ? z : -INFINITY;
+            }
+        }
+    }
+}
+
+template <int DT, bool VEC, int EPT>
+__device__ __forceinline__ void load_chunk(const void* rowp, int v0, int V, float (&x)[EPT])
+{
+    if (v0 + EPT * kThreads <= V) load_chunk_impl<DT, VEC, EPT, true>(rowp, v0, V, x);
+    else load_chunk_impl<DT, VEC, EPT, false>(rowp, v0, V, x);
+}
+
+template <bool VEC, int EPT, int W>
+__device__ __forceinline__ int elem_index(int v0, int e)
+{
+    if constexpr (VEC) return v0 + ((e / W) * kThreads + (int)threadIdx.x) * W + (e % W);
+    else return v0 + e * kThreads + (int)threadIdx.x;
+}
+
+struct RowParams {
+    const void* logits;
+    const void* probs;
+    const int32_t* tokens;
+    const float* uniforms;
+    uint64_t* mask;
+    uint32_t* cnt1;
+    uint64_t* part1;  // [rows][nch][2]
+    RowStat* stats;
+    int B, gamma, V, nch, probs_dtype;
+    uint32_t zero;     // always 0 (see publish)
+    float c_hi, c_lo;  // log2(e)/T split into two fp32 terms, c_lo > 0
+    double cd;         // log2(e)/T in double
+};
+
+// Shared prologue: is this (row, chunk) still needed?  Thread 0 reads the
+// sequence's reject mask once and broadcasts, so the whole block agrees.
+__device__ __forceinline__ bool chunk_skipped(const RowParams& p, int b, int k, int* sm_flag)
+{
+    if (threadIdx.x == 0) {
+        const uint64_t m = ld_agent(&p.mask[b]);
+        const uint64_t earlier = k == 0 ? 0ull : (m & ((1ull << k) - 1ull));
+        *sm_flag = ((m & kInvalidBit) | earlier) ? 1 : 0;
+    }
+    __syncthreads();
+    return *sm_flag != 0;
+}
+
+// Shared epilogue: count this block in and learn whether it is the last
+// block of the row (returns 0: not last, 1: last and every chunk was done,
+// 2: last but some chunk was skipped).  The counter keeps arrivals in its low
+// 16 bits and skips in its high bits; the last block resets it to zero.
+__device__ __forceinline__ int row_arrive(const RowParams& p, int64_t row, bool skip, uint32_t dep, int* sm_flag)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t inc = (skip ? 0x10001u : 1u) + dep;
+        const uint32_t old = __hip_atomic_fetch_add(&p.cnt1[row], inc, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = (old & 0xffffu) + 1u == (uint32_t)p.nch;
+        const bool any_skip = skip || (old >> 16) != 0u;
+        if (last) __hip_atomic_store(&p.cnt1[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *sm_flag = last ? (any_skip ? 2 : 1) : 0;
+    }
+    __syncthreads();
+    return *sm_flag;
+}
+
+// The last block of a row clears the row's partial slots once it has read
+// them, so that a finished call leaves the whole workspace zero (a later
+// call with another shape may place its counters there).
+__device__ __forceinline__ void clear_row_partials(const RowParams& p, int64_t row)
+{
+    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+        uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
+        st_agent(slot, 0ull);
+        st_agent(slot + 1, 0ull);
+    }
+}
+
+// ----------------------------------------------------------------- row stage, sample
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
+{
+    constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
+    constexpr int CH = EPT * kThreads;
+    const int c = (int)(blockIdx.x % (unsigned)p.nch);
+    const int t = (int)(blockIdx.x / (unsigned)p.nch);
+    const int b = t % p.B;
+    const int k = t / p.B;
+    const int G1 = p.gamma + 1;
+    const int64_t row = (int64_t)b * G1 + k;
+
+    __shared__ float sm_f[kWaves];
+    __shared__ double sm_d[kWaves];
+    __shared__ int sm_flag;
+
+    const bool skip = chunk_skipped(p, b, k, &sm_flag);
+    uint32_t dep = 0;
+    if (!skip) {
+        const int v0 = c * CH;
+        const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
+        float x[EPT];
+        load_chunk<DT, VEC, EPT>(rowp, v0, p.V, x);
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, x[e]);
+        mx = block_max(mx, sm_f);
+
+        double s = 0.0;
+        double mc = 0.0;
+        float K = 0.0f;
+        if (mx > -INFINITY) {
+            // exponent of element z: z*c_hi + K + z*c_lo = (z - mx)*log2(e)/T + eta,
+            // with eta = K + mx*cd the rounding of the shift (corrected below).
+            mc = (double)mx * p.cd;
+            K = (float)(-mc);
+            double acc = 0.0;
+#pragma unroll
+            for (int g = 0; g < EPT / 8; ++g) {
+                float e8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float z = x[g * 8 + e];
+                    e8[e] = __builtin_amdgcn_exp2f(fmaf(z, p.c_lo, fmaf(z, p.c_hi, K)));
+                }
+                acc += (double)(((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7])));
+            }
+            s = block_sum(acc, sm_d);
+        }
+        if (threadIdx.x == 0) {
+            if (mx > -INFINITY) s *= exp2(-((double)K + mc));
+            const uint64_t w[2] = {(uint64_t)__float_as_uint(mx), (uint64_t)__double_as_longlong(s)};
+            dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
+        }
+    }
+
+    const int arrival = row_arrive(p, row, skip, dep, &sm_flag);
+    if (arrival == 0) return;
+    if (arrival == 2) {  // row not needed: an earlier position was rejected
+        clear_row_partials(p, row);
+        return;
+    }
+
+    // Last block of a fully processed row: merge the chunk partials.
+    float M = -INFINITY;
+    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
+        M = fmaxf(M, __uint_as_float((uint32_t)ld_agent(slot)));
+    }
+    M = block_max(M, sm_f);
+    double S = 0.0;
+    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
+        const float mj = __uint_as_float((uint32_t)ld_agent(slot));
+        const double sj = __longlong_as_double((long long)ld_agent(slot + 1));
+        if (mj > -INFINITY) S += sj * exp2(((double)mj - (double)M) * p.cd);
+    }
+    S = block_sum(S, sm_d);  // (its barriers end every read of the slots)
+    clear_row_partials(p, row);
+
+    if (threadIdx.x == 0) {
+        RowStat st;
+        st.m = M;
+        st.amax = -1;
+        st.S = S;
+        st.P = NAN;
+        st.Q = NAN;
+        if (k < p.gamma) {
+            // [FI] Phase 3 / [PB] section 3: accept x_k iff u_k <= min(1, p/q),
+            // q <= 0 accepts ([PB] Reference Implementation).
+            const int x = p.tokens[(int64_t)b * p.gamma + k];
+            if (x < 0 || x >= p.V) {
+                __hip_atomic_fetch_or(&p.mask[b], kInvalidBit | (1ull << k), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                const double z = (double)load_one_rt(p.logits, DT, row * p.V + x);
+                const double P = exp2((z - (double)M) * p.cd) / S;
+                const double Q = (double)load_one_rt(p.probs, p.probs_dtype,
+                                                     ((int64_t)b * p.gamma + k) * p.V + x);
+                const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / Q);
+                const double u = (double)p.uniforms[(int64_t)b * G1 + k];
+                st.P = P;
+                st.Q = Q;
+                if (!(u <= thr))
+                    __hip_atomic_fetch_or(&p.mask[b], 1ull << k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        p.stats[row] = st;
+    }
+}
+
+// ----------------------------------------------------------------- row stage, greedy
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
+{
+    constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
+    constexpr int W = DT == SV_BF16 ? 8 : 4;
+    constexpr int CH = EPT * kThreads;
+    const int c = (int)(blockIdx.x % (unsigned)p.nch);
+    const int t = (int)(blockIdx.x / (unsigned)p.nch);
+    const int b = t % p.B;
+    const int k = t / p.B;
+    const int G1 = p.gamma + 1;
+    const int64_t row = (int64_t)b * G1 + k;
+
+    __shared__ float sm_f[kWaves];
+    __shared__ int sm_i[kWaves];
+    __shared__ int sm_flag;
+
+    const bool skip = chunk_skipped(p, b, k, &sm_flag);
+    uint32_t dep = 0;
+    if (!skip) {
+        const int v0 = c * CH;
+        const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
+        float x[EPT];
+        load_chunk<DT, VEC, EPT>(rowp, v0, p.V, x);
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int idx = elem_index<VEC, EPT, W>(v0, e);
+            if (idx < p.V) amax_merge(bv, bi, x[e], idx);
+        }
+        block_amax(bv, bi, sm_f, sm_i);
+        if (threadIdx.x == 0) {
+            const uint64_t w[1] = {((uint64_t)(uint32_t)bi << 32) | (uint64_t)__float_as_uint(bv)};
+            dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
+        }
+    }
+
+    const int arrival = row_arrive(p, row, skip, dep, &sm_flag);
+    if (arrival == 0) return;
+    if (arrival == 2) {
+        clear_row_partials(p, row);
+        return;
+    }
+
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+        const uint64_t w = ld_agent(p.part1 + 2 * ((size_t)row * p.nch + j));
+        amax_merge(bv, bi, __uint_as_float((uint32_t)w), (int)(uint32_t)(w >> 32));
+    }
+    block_amax(bv, bi, sm_f, sm_i);
+    clear_row_partials(p, row);
+    if (threadIdx.x == 0) {
+        RowStat st;
+        st.m = bv;
+        st.amax = bi;
+        st.S = NAN;
+        st.P = NAN;
+        st.Q = NAN;
+        if (k < p.gamma) {
+            // [FI] "Standardized Sampling", argmax case: the draft survives iff
+            // it is the target argmax.
+            const int x = p.tokens[(int64_t)b * p.gamma + k];
+            uint64_t bits = 0;
+            if (x < 0 || x >= p.V) bits = kInvalidBit | (1ull << k);
+            else if (x != bi) bits = 1ull << k;
+            if (bits) __hip_atomic_fetch_or(&p.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        p.stats[row] = st;
+    }
+}
+
+// ------------------------------------------------------------------- draw stage
+
+struct DrawParams {
+    const void* logits;
+    const void* probs;
+    const int32_t* tokens;
+    const float* uniforms;
+    uint64_t* mask;
+    uint32_t* cnt2;
+    RowStat* stats;
+    DrawPart* part2;  // [B][nch2]
+    int32_t* n_out;
+    int32_t* tok_out;
+    double* aux_p;
+    double* aux_q;
+    double* aux_resid;
+    float* aux_rmax;
+    double* aux_rsum;
+    int B, gamma, V, nch2;
+    uint32_t zero;  // always 0 (see publish)
+    double cd;
+};
+
+// Writes the per-sequence outputs and telemetry, and clears the sequence's
+// reject mask for the next call.  Called by the whole block.
+__device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool invalid, double Z, bool sample)
+{
+    const int G1 = p.gamma + 1;
+    for (int i = threadIdx.x; i < G1; i += kThreads) {
+        int32_t o;
+        if (invalid) o = -1;
+        else if (i < n) o = p.tokens[(int64_t)b * p.gamma + i];
+        else if (i == n) o = t;
+        else o = -1;
+        p.tok_out[(int64_t)b * G1 + i] = o;
+        const RowStat st = p.stats[(int64_t)b * G1 + i];
+        p.stats[(int64_t)b * G1 + i] = RowStat{0.0f, 0, 0.0, 0.0, 0.0};  // leave the workspace zero
+        const bool row_seen = !invalid && i <= n;
+        if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + i] = row_seen ? st.m : NAN;
+        if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + i] = (row_seen && sample) ? st.S : NAN;
+        if (i < p.gamma) {
+            const bool tested = sample && row_seen;
+            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + i] = tested ? st.P : NAN;
+            if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + i] = tested ? st.Q : NAN;
+        }
+    }
+    if (threadIdx.x == 0) {
+        p.n_out[b] = invalid ? -1 : n;
+        if (p.aux_resid) p.aux_resid[b] = (!invalid && sample && n < p.gamma) ? Z : NAN;
+        p.mask[b] = 0ull;
+    }
+}
+
+__device__ __forceinline__ void clear_draw_partials(const DrawParams& p, int b)
+{
+    for (int j = threadIdx.x; j < p.nch2; j += kThreads) {
+        uint64_t* slot = reinterpret_cast<uint64_t*>(p.part2 + (size_t)b * p.nch2 + j);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) st_agent(slot + w, 0ull);
+    }
+}
+
+// Any draft token of sequence b outside [0, V)?  (Checked over all gamma
+// tokens, also those past the first rejection.)
+__device__ bool tokens_invalid(const DrawParams& p, int b, int* sm_i)
+{
+    int bad = 0;
+    for (int i = threadIdx.x; i < p.gamma; i += kThreads) {
+        const int x = p.tokens[(int64_t)b * p.gamma + i];
+        bad |= (x < 0 || x >= p.V) ? 1 : 0;
+    }
+    return block_max_i(bad, sm_i) != 0;
+}
+
+// 2^a in double for any a <= 0 (including -inf), accurate to a few ulp:
+// a = (k + f) / 64 with k integer and |f| <= 1/2, 2^a = 2^(k >> 6) *
+// 2^((k & 63)/64) * exp(f ln2 / 64); the middle factor comes from a 64-entry
+// table in LDS and the last from its degree-5 Taylor polynomial (remainder
+// below 4e-17).
+__device__ __forceinline__ double exp2_tab(double a, const double* tab)
+{
+    a = fmax(a, -1100.0);  // -inf and huge negatives: the ldexp underflows to 0
+    const double t = a * 64.0;
+    const double kf = rint(t);
+    const double r = (t - kf) * 0.010830424696249145;  // ln(2) / 64
+    const int k = (int)kf;
+    double poly = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+    poly = fma(r, poly, 1.0 / 6.0);
+    poly = fma(r, poly, 0.5);
+    poly = fma(r, poly, 1.0);
+    poly = fma(r, poly, 1.0);
+    return ldexp(tab[k & 63] * poly, k >> 6);
+}
+
+// Loads 8 consecutive elements starting at idx (a multiple of 8 on the
+// vector path).  Past-the-end elements read as `pad`.
+template <int DT, bool VEC, bool FULL>
+__device__ __forceinline__ void load8(const void* rowp, int idx, int V, float pad, float* out)
+{
+    constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
+    if constexpr (VEC) {
+        const int ci = FULL ? idx : min(idx, V - 8);
+        const char* ptr = static_cast<const char*>(rowp) + (size_t)ci * ES;
+        if constexpr (DT == SV_BF16) {
+            const uint4 w = *reinterpret_cast<const uint4*>(ptr);
+            out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+            out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+        } else {
+            const uint4 a = *reinterpret_cast<const uint4*>(ptr);
+            const uint4 b = *reinterpret_cast<const uint4*>(ptr + 16);
+            out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
+            out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
+            out[4] = __uint_as_float(b.x); out[5] = __uint_as_float(b.y);
+            out[6] = __uint_as_float(b.z); out[7] = __uint_as_float(b.w);
+        }
+        if constexpr (!FULL) {
+            if (idx >= V) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out[e] = pad;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = idx + e;
+            if constexpr (FULL) {
+                out[e] = load_one<DT>(rowp, i);
+            } else {
+                const float v = load_one<DT>(rowp, min(i, V - 1));
+                out[e] = i < V ? v : pad;
+            }
+        }
+    }
+}
+
+// Chunk sums of the draw stage for this thread's 16 elements: groups of 8
+// consecutive elements at v0 + (g * kThreads + tid) * 8, g = 0, 1.
+template <int DT, int PT, bool VEC, bool FULL>
+__device__ __forceinline__ void draw_chunk_sums(const DrawParams& p, const void* zrow, const void* qrow,
+                                                bool resid, int v0, double M, double S_row,
+                                                const double* tab, double& E, double& EA, double& QA,
+                                                int& lastA, int& lastE)
+{
+    float z[kEpt2], q[kEpt2];
+#pragma unroll
+    for (int g = 0; g < kEpt2 / 8; ++g)
+        load8<DT, VEC, FULL>(zrow, v0 + (g * kThreads + (int)threadIdx.x) * 8, p.V, -INFINITY, z + g * 8);
+    if (resid) {
+#pragma unroll
+        for (int g = 0; g < kEpt2 / 8; ++g)
+            load8<PT, VEC, FULL>(qrow, v0 + (g * kThreads + (int)threadIdx.x) * 8, p.V, 0.0f, q + g * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kEpt2; ++i) {
+        const int v = v0 + ((i / 8) * kThreads + (int)threadIdx.x) * 8 + (i % 8);
+        const double e = exp2_tab(((double)z[i] - M) * p.cd, tab);
+        E += e;
+        if (e > 0.0) lastE = v;
+        if (resid) {
+            const double qd = (double)q[i];
+            if (e > qd * S_row) { EA += e; QA += qd; lastA = v; }
+        }
+    }
+}
+
+// The weights of one thread's contiguous run of 16 elements, [v0, v0 + 16),
+// for the inverse-CDF scan: max(0, p_v - q_v) or e_v.
+template <int DT, int PT, bool VEC, bool FULL>
+__device__ __forceinline__ void draw_run_weights(const DrawParams& p, const void* zrow, const void* qrow,
+                                                 bool use_resid, int v0, double M, double S,
+                                                 const double* tab, double (&w)[kEpt2])
+{
+    float z[kEpt2], q[kEpt2];
+#pragma unroll
+    for (int g = 0; g < kEpt2 / 8; ++g) load8<DT, VEC, FULL>(zrow, v0 + g * 8, p.V, -INFINITY, z + g * 8);
+    if (use_resid) {
+#pragma unroll
+        for (int g = 0; g < kEpt2 / 8; ++g) load8<PT, VEC, FULL>(qrow, v0 + g * 8, p.V, 0.0f, q + g * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kEpt2; ++i) {
+        const double e = exp2_tab(((double)z[i] - M) * p.cd, tab);
+        w[i] = use_resid ? fmax(0.0, e / S - (double)q[i]) : e;
+        if (v0 + i >= p.V) w[i] = 0.0;
+    }
+}
+
+__device__ __forceinline__ const uint64_t* draw_slot(const DrawParams& p, int b, int j)
+{
+    return reinterpret_cast<const uint64_t*>(p.part2 + (size_t)b * p.nch2 + j);
+}
+__device__ __forceinline__ double slot_d(const uint64_t* s, int w)
+{
+    return __longlong_as_double((long long)ld_agent(s + w));
+}
+
+template <int DT, int PT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draw_sample(const DrawParams p)
+{
+    const int b = (int)(blockIdx.x / (unsigned)p.nch2);
+    const int c = (int)(blockIdx.x % (unsigned)p.nch2);
+    const int G1 = p.gamma + 1;
+
+    __shared__ double tab[64];
+    __shared__ double sm_d[kWaves];
+    __shared__ int sm_i[kWaves];
+    __shared__ int sm_flag;
+    __shared__ double sm_pre;
+
+    if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
+
+    const uint64_t m = p.mask[b];
+    const bool invalid_seen = (m & kInvalidBit) != 0;
+    const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
+    const int n = rej ? __builtin_ctzll(rej) : p.gamma;
+    const bool resid = n < p.gamma;
+    const int64_t row = (int64_t)b * G1 + n;
+    const int64_t qrow_i = (int64_t)b * p.gamma + n;
+    const RowStat st = p.stats[row];  // in bounds for any mask (n <= gamma)
+    const double M = (double)st.m;
+    const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+    const void* qrow = resid ? static_cast<const char*>(p.probs) + (size_t)qrow_i * p.V * (PT == SV_BF16 ? 2 : 4)
+                             : nullptr;
+    __syncthreads();  // table ready
+
+    uint32_t dep = 0;
+    if (!invalid_seen) {
+        double E = 0.0, EA = 0.0, QA = 0.0;
+        int lastA = -1, lastE = -1;
+        const int v0 = c * kChunk2;
+        // st.S (row stage) only decides which elements lie in the residual
+        // support; the normaliser itself is re-summed in fp64 below.
+        if (v0 + kChunk2 <= p.V)
+            draw_chunk_sums<DT, PT, VEC, true>(p, zrow, qrow, resid, v0, M, st.S, tab, E, EA, QA, lastA, lastE);
+        else
+            draw_chunk_sums<DT, PT, VEC, false>(p, zrow, qrow, resid, v0, M, st.S, tab, E, EA, QA, lastA, lastE);
+        E = block_sum(E, sm_d);
+        EA = block_sum(EA, sm_d);
+        QA = block_sum(QA, sm_d);
+        lastA = block_max_i(lastA, sm_i);
+        lastE = block_max_i(lastE, sm_i);
+        if (threadIdx.x == 0) {
+            const uint64_t w[4] = {(uint64_t)__double_as_longlong(E), (uint64_t)__double_as_longlong(EA),
+                                   (uint64_t)__double_as_longlong(QA),
+                                   ((uint64_t)(uint32_t)lastE << 32) | (uint64_t)(uint32_t)lastA};
+            dep = publish(reinterpret_cast<uint64_t*>(p.part2 + (size_t)b * p.nch2 + c), w, p.zero);
+        }
+    }
+
+    // arrival count; the last block of the sequence finishes it
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&p.cnt2[b], 1u + dep, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old + 1u == (uint32_t)p.nch2;
+        if (last) __hip_atomic_store(&p.cnt2[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (sm_flag == 0) return;
+
+    const bool bad_token = tokens_invalid(p, b, sm_i);  // called by every thread (barriers)
+    const bool invalid = invalid_seen || bad_token;
+    if (invalid) {
+        clear_draw_partials(p, b);
+        finish_sequence(p, b, n, -1, true, NAN, true);
+        return;
+    }
+
+    // exact normaliser of row n and the residual mass, from the chunk sums
+    double S = 0.0;
+    for (int j = threadIdx.x; j < p.nch2; j += kThreads) S += slot_d(draw_slot(p, b, j), 0);
+    S = block_sum(S, sm_d);
+    double Z = 0.0;
+    if (resid) {
+        for (int j = threadIdx.x; j < p.nch2; j += kThreads) {
+            const uint64_t* sl = draw_slot(p, b, j);
+            Z += fmax(0.0, slot_d(sl, 1) / S - slot_d(sl, 2));
+        }
+        Z = block_sum(Z, sm_d);
+    }
+    // [FI] Phase 4: residual norm(max(0, p_n - q_n)) after a rejection, with
+    // [ST]'s fallback to p_n; the bonus row p_gamma after full acceptance.
+    const bool use_resid = resid && Z > kResidEps;
+    const double total = use_resid ? Z : S;
+    const double target = (double)p.uniforms[(int64_t)b * G1 + p.gamma] * total;
+
+    // the first chunk whose running weight sum exceeds the target (block scan
+    // over the chunk weights, 256 chunks per round)
+    int jc = -1;
+    double carry = 0.0;
+    for (int j0 = 0; j0 < p.nch2 && jc < 0; j0 += kThreads) {
+        const int j = j0 + (int)threadIdx.x;
+        double w = 0.0;
+        if (j < p.nch2) {
+            const uint64_t* sl = draw_slot(p, b, j);
+            w = use_resid ? fmax(0.0, slot_d(sl, 1) / S - slot_d(sl, 2)) : slot_d(sl, 0);
+        }
+        double tot;
+        const double excl = block_exclusive_scan(w, sm_d, &tot);
+        const bool hit = j < p.nch2 && w > 0.0 && carry + excl + w > target;
+        const int first = block_min_i(hit ? j : INT_MAX, sm_i);
+        if (first != INT_MAX) {
+            if (j == first) sm_pre = carry + excl;
+            __syncthreads();
+            jc = first;
+            carry = sm_pre;
+            __syncthreads();
+        } else {
+            carry += tot;
+        }
+    }
+    double rem = target - carry;  // target relative to the start of chunk jc
+
+    // scan chunk jc (and, only if rounding pushed the crossing out of it, the
+    // chunks after it): thread t owns the contiguous run [16 t, 16 t + 16)
+    int tok = -1;
+    while (jc >= 0 && jc < p.nch2 && tok < 0) {
+        const int base = jc * kChunk2 + (int)threadIdx.x * kEpt2;
+        double w[kEpt2];
+        if (jc * kChunk2 + kChunk2 <= p.V)
+            draw_run_weights<DT, PT, VEC, true>(p, zrow, qrow, use_resid, base, M, S, tab, w);
+        else
+            draw_run_weights<DT, PT, VEC, false>(p, zrow, qrow, use_resid, base, M, S, tab, w);
+        double local = 0.0;
+#pragma unroll
+        for (int i = 0; i < kEpt2; ++i) local += w[i];
+        double ctot;
+        const double excl = block_exclusive_scan(local, sm_d, &ctot);
+        int cand = INT_MAX;
+        if (excl + local > rem) {
+            double cum = excl;
+#pragma unroll
+            for (int i = 0; i < kEpt2; ++i) {
+                cum += w[i];
+                if (cand == INT_MAX && w[i] > 0.0 && cum > rem) cand = base + i;
+            }
+        }
+        cand = block_min_i(cand, sm_i);
+        if (cand != INT_MAX) tok = cand;
+        rem -= ctot;
+        ++jc;
+    }
+    if (tok < 0) {
+        // u * total at or past the end: largest index with positive weight
+        int lastv = -1;
+        for (int j = threadIdx.x; j < p.nch2; j += kThreads) {
+            const uint64_t w = ld_agent(draw_slot(p, b, j) + 3);
+            lastv = max(lastv, use_resid ? (int)(int32_t)(uint32_t)w : (int)(int32_t)(uint32_t)(w >> 32));
+        }
+        tok = block_max_i(lastv, sm_i);
+    }
+    // every read of this sequence's chunk slots ended before a barrier above
+    clear_draw_partials(p, b);
+    finish_sequence(p, b, n, tok, false, Z, true);
+}
+
+__global__ __launch_bounds__(kThreads) void k_draw_greedy(const DrawParams p)
+{
+    // one block per sequence: n is the first rejected position, the token the
+    // argmax of row n ([FI] "Standardized Sampling", argmax case)
+    const int b = blockIdx.x;
+    __shared__ int sm_i[kWaves];
+    const uint64_t m = p.mask[b];
+    const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
+    const int n = rej ? __builtin_ctzll(rej) : p.gamma;
+    // every thread reads the mask before the barriers in tokens_invalid, and
+    // the mask is cleared only after them (finish_sequence)
+    const bool bad_token = tokens_invalid(p, b, sm_i);
+    const bool invalid = (m & kInvalidBit) != 0 || bad_token;
+    const int t = invalid ? -1 : p.stats[(int64_t)b * (p.gamma + 1) + n].amax;
+    finish_sequence(p, b, n, t, invalid, NAN, false);
+}
+
+__global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < ntail) tail[i] = 0;
+}
+
+// ---------------------------------------------------------------- host dispatch
+
+template <int DT>
+void launch_rows(bool greedy, bool vec, int grid, const RowParams& rp, hipStream_t s)
+{
+    if (greedy) {
+        if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true>), dim3(grid), dim3(kThreads), 0, s, rp);
+        else hipLaunchKernelGGL((k_rows_greedy<DT, false>), dim3(grid), dim3(kThreads), 0, s, rp);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_rows_sample<DT, true>), dim3(grid), dim3(kThreads), 0, s, rp);
+        else hipLaunchKernelGGL((k_rows_sample<DT, false>), dim3(grid), dim3(kThreads), 0, s, rp);
+    }
+}
+
+template <int DT, int PT>
+void launch_draw_sample_t(bool vec, int grid, const DrawParams& dp, hipStream_t s)
+{
+    if (vec) hipLaunchKernelGGL((k_draw_sample<DT, PT, true>), dim3(grid), dim3(kThreads), 0, s, dp);
+    else hipLaunchKernelGGL((k_draw_sample<DT, PT, false>), dim3(grid), dim3(kThreads), 0, s, dp);
+}
+
+void launch_draw_sample(int dt, int pt, bool vec, int grid, const DrawParams& dp, hipStream_t s)
+{
+    if (dt == SV_FP32 && pt == SV_FP32) launch_draw_sample_t<SV_FP32, SV_FP32>(vec, grid, dp, s);
+    if (dt == SV_FP32 && pt == SV_BF16) launch_draw_sample_t<SV_FP32, SV_BF16>(vec, grid, dp, s);
+    if (dt == SV_BF16 && pt == SV_FP32) launch_draw_sample_t<SV_BF16, SV_FP32>(vec, grid, dp, s);
+    if (dt == SV_BF16 && pt == SV_BF16) launch_draw_sample_t<SV_BF16, SV_BF16>(vec, grid, dp, s);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_bytes(int batch, int gamma, int vocab)
+{
+    if (batch < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || vocab < 1) return 0;
+    return make_layout(batch, gamma, vocab).total;
+}
+
+int sv_workspace_init(void* workspace, size_t bytes, void* stream)
+{
+    if (!workspace) return SV_ERR_NULL_POINTER;
+    if (!aligned(workspace, 256)) return SV_ERR_ALIGNMENT;
+    if (bytes == 0) return SV_OK;
+    const size_t n16 = bytes / 16, ntail = bytes % 16;
+    const size_t threads = n16 > ntail ? n16 : ntail;
+    const size_t blocks = (threads + 255) / 256;
+    if (blocks > (size_t)INT_MAX) return SV_ERR_TOO_LARGE;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<uint4*>(workspace), n16,
+                       static_cast<unsigned char*>(workspace) + n16 * 16, ntail);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+int spec_verify(int batch, int gamma, int vocab,
+                const void* target_logits, int logits_dtype,
+                const void* draft_probs, int probs_dtype,
+                const int32_t* draft_tokens, const float* uniforms,
+                float temperature, int mode,
+                int32_t* n_accepted, int32_t* out_tokens,
+                void* workspace, size_t workspace_bytes,
+                const sv_extras_t* extras, void* stream)
+{
+    // ---- argument validation (no HIP call before this block passes)
+    if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_ERR_MODE;
+    if (batch < 1) return SV_ERR_BATCH;
+    if (gamma < 1 || gamma > SV_MAX_GAMMA) return SV_ERR_GAMMA;
+    if (vocab < 1) return SV_ERR_VOCAB;
+    if (logits_dtype != SV_FP32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+    const bool greedy = mode == SV_GREEDY;
+    if (!target_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_ERR_NULL_POINTER;
+    if (!greedy) {
+        if (!draft_probs || !uniforms) return SV_ERR_NULL_POINTER;
+        if (probs_dtype != SV_FP32 && probs_dtype != SV_BF16) return SV_ERR_DTYPE;
+        if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SV_ERR_TEMPERATURE;
+    }
+    const size_t lsz = logits_dtype == SV_BF16 ? 2 : 4;
+    const size_t psz = probs_dtype == SV_BF16 ? 2 : 4;
+    if (!aligned(target_logits, lsz) || !aligned(draft_tokens, 4) || !aligned(n_accepted, 4) ||
+        !aligned(out_tokens, 4))
+        return SV_ERR_ALIGNMENT;
+    if (!greedy && (!aligned(draft_probs, psz) || !aligned(uniforms, 4))) return SV_ERR_ALIGNMENT;
+    const Layout L = make_layout(batch, gamma, vocab);
+    if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SV_ERR_ALIGNMENT;
+
+    const int G1 = gamma + 1;
+    const int chunk1 = logits_dtype == SV_BF16 ? kChunkBf16 : kChunkFp32;
+    const int nch1 = (vocab + chunk1 - 1) / chunk1;
+    const long long grid1 = (long long)G1 * batch * nch1;
+    if (nch1 > 0xffff || grid1 > INT_MAX) return SV_ERR_TOO_LARGE;
+    const bool vec = aligned(target_logits, 16) && ((size_t)vocab * lsz) % 16 == 0;
+
+    const int nch2 = (vocab + kChunk2 - 1) / kChunk2;
+    // draw-stage vector loads need 16-byte aligned rows in both tensors
+    const bool vec2 = vocab % 8 == 0 && aligned(target_logits, 16) && (greedy || aligned(draft_probs, 16));
+    const long long grid2 = greedy ? (long long)batch : (long long)batch * nch2;
+    if (grid2 > INT_MAX) return SV_ERR_TOO_LARGE;
+
+    char* ws = static_cast<char*>(workspace);
+    hipStream_t s = (hipStream_t)stream;
+
+    // log2(e)/T as c_hi + c_lo with c_hi <= log2(e)/T, so c_lo > 0 and
+    // -inf logits stay -inf through both fused multiply-adds
+    const double cd = greedy ? 0.0 : kLog2e / (double)temperature;
+    float c_hi = (float)cd;
+    if ((double)c_hi >= cd) c_hi = std::nextafter(c_hi, 0.0f);
+    const float c_lo = (float)(cd - (double)c_hi);
+
+    RowParams rp;
+    rp.logits = target_logits;
+    rp.probs = draft_probs;
+    rp.tokens = draft_tokens;
+    rp.uniforms = uniforms;
+    rp.mask = reinterpret_cast<uint64_t*>(ws + L.mask_off);
+    rp.cnt1 = reinterpret_cast<uint32_t*>(ws + L.cnt1_off);
+    rp.part1 = reinterpret_cast<uint64_t*>(ws + L.part1_off);
+    rp.stats = reinterpret_cast<RowStat*>(ws + L.stats_off);
+    rp.B = batch;
+    rp.gamma = gamma;
+    rp.V = vocab;
+    rp.nch = nch1;
+    rp.probs_dtype = probs_dtype;
+    rp.zero = 0u;
+    rp.c_hi = c_hi;
+    rp.c_lo = c_lo;
+    rp.cd = cd;
+
+    DrawParams dp;
+    dp.logits = target_logits;
+    dp.probs = draft_probs;
+    dp.tokens = draft_tokens;
+    dp.uniforms = uniforms;
+    dp.mask = rp.mask;
+    dp.cnt2 = reinterpret_cast<uint32_t*>(ws + L.cnt2_off);
+    dp.stats = rp.stats;
+    dp.part2 = reinterpret_cast<DrawPart*>(ws + L.part2_off);
+    dp.n_out = n_accepted;
+    dp.tok_out = out_tokens;
+    dp.aux_p = extras ? extras->p_tok : nullptr;
+    dp.aux_q = extras ? extras->q_tok : nullptr;
+    dp.aux_resid = extras ? extras->resid_mass : nullptr;
+    dp.aux_rmax = extras ? extras->row_max : nullptr;
+    dp.aux_rsum = extras ? extras->row_sum : nullptr;
+    dp.B = batch;
+    dp.gamma = gamma;
+    dp.V = vocab;
+    dp.nch2 = nch2;
+    dp.zero = 0u;
+    dp.cd = cd;
+
+    if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)
+        return SV_ERR_LAUNCH;
+    if (logits_dtype == SV_BF16) launch_rows<SV_BF16>(greedy, vec, (int)grid1, rp, s);
+    else launch_rows<SV_FP32>(greedy, vec, (int)grid1, rp, s);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    if (extras && extras->ev_mid && hipEventRecord((hipEvent_t)extras->ev_mid, s) != hipSuccess)
+        return SV_ERR_LAUNCH;
+    if (greedy) hipLaunchKernelGGL(k_draw_greedy, dim3((unsigned)grid2), dim3(kThreads), 0, s, dp);
+    else launch_draw_sample(logits_dtype, probs_dtype, vec2, (int)grid2, dp, s);
+    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    if (extras && extras->ev_end && hipEventRecord((hipEvent_t)extras->ev_end, s) != hipSuccess)
+        return SV_ERR_LAUNCH;
+    return SV_OK;
+}
+
+const char* sv_status_string(int status)
+{
+    switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case SV_ERR_BATCH: return "batch must be >= 1";
+    case SV_ERR_GAMMA: return "gamma must be in [1, SV_MAX_GAMMA]";
+    case SV_ERR_VOCAB: return "vocab must be >= 1";
+    case SV_ERR_TEMPERATURE: return "temperature must be finite and > 0 in sample mode";
+    case SV_ERR_DTYPE: return "dtype must be SV_FP32 or SV_BF16";
+    case SV_ERR_MODE: return "mode must be SV_SAMPLE or SV_GREEDY";
+    case SV_ERR_WORKSPACE: return "workspace is NULL or smaller than sv_workspace_bytes()";
+    case SV_ERR_ALIGNMENT: return "a pointer is misaligned for its element type, or the workspace is not 256-byte aligned";
+    case SV_ERR_TOO_LARGE: return "problem exceeds the launch-grid limits";
+    case SV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

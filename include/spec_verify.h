@@ -1,0 +1,142 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X (gfx950) verify-and-sample library
+ * for speculative decoding.
+ *
+ * The operation ("Fast Inference from Transformers via Speculative
+ * Decoding", paper summary page, "Speculative Sampling: The Core
+ * Algorithm", Algorithm 1 Phases 3 and 4; "Speculative Decoding Paper
+ * Breakdown: Lossless Draft-and-Verify Acceleration for Autoregressive
+ * Transformers", section 3 "The Algorithm at Position i"; "Speculative
+ * Decoding: Two Models, One Output", "The algorithm"):
+ *
+ *   for each sequence b, positions i = 0 .. gamma-1 in order:
+ *     p_i = softmax(target_logits[b][i] / T)           ("Standardized Sampling")
+ *     accept x_i iff u_i <= min(1, p_i(x_i) / q_i(x_i))  (q_i(x_i) <= 0: accept)
+ *     stop at the first rejection; n = number accepted (0 .. gamma)
+ *   if n < gamma: t ~ norm(max(0, p_n - q_n)), or t ~ p_n when that residual
+ *                 mass is <= 1e-15 ("The exact decoding shortcut that burns
+ *                 compute when guesses miss", correction_distribution)
+ *   if n == gamma: bonus token t ~ p_gamma
+ *   emit x_0 .. x_{n-1}, t   (between 1 and gamma+1 tokens)
+ *
+ * Draws use the caller's uniforms: u_i = uniforms[b][i] for the acceptance
+ * test at position i, u_gamma = uniforms[b][gamma] for the one final draw,
+ * by inverse CDF (the smallest k whose running weight sum exceeds
+ * u * total).  In greedy mode every distribution is the point mass at the
+ * first index attaining the row maximum of the raw logits ("Standardized
+ * Sampling", argmax case): a draft survives iff it equals that argmax and
+ * the emitted token is the argmax of the row where the walk stopped.
+ *
+ * Every tensor argument is a DEVICE pointer on the current HIP device,
+ * row-major and contiguous, owned by the caller.  The library never
+ * allocates, frees or synchronises; a call only enqueues kernels on
+ * `stream` (a hipStream_t; NULL = the default stream) and returns.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  SV_BF16 data are raw bfloat16 bit patterns (uint16). */
+#define SV_FP32 0
+#define SV_BF16 1
+
+/* Modes. */
+#define SV_SAMPLE 0 /* temperature sampling, exact rejection rule            */
+#define SV_GREEDY 1 /* argmax standardisation; T, draft_probs, uniforms unused */
+
+/* Largest supported gamma (one bit per draft position in a 64-bit word). */
+#define SV_MAX_GAMMA 62
+
+/* Status codes returned synchronously by every entry point. */
+#define SV_OK 0
+#define SV_ERR_NULL_POINTER -1  /* a required pointer is NULL                        */
+#define SV_ERR_BATCH -2         /* batch < 1                                         */
+#define SV_ERR_GAMMA -3         /* gamma < 1 or gamma > SV_MAX_GAMMA                 */
+#define SV_ERR_VOCAB -4         /* vocab < 1                                         */
+#define SV_ERR_TEMPERATURE -5   /* sample mode with temperature <= 0 or not finite  */
+#define SV_ERR_DTYPE -6         /* dtype tag is neither SV_FP32 nor SV_BF16          */
+#define SV_ERR_MODE -7          /* mode is neither SV_SAMPLE nor SV_GREEDY           */
+#define SV_ERR_WORKSPACE -8     /* workspace NULL or smaller than sv_workspace_bytes */
+#define SV_ERR_ALIGNMENT -9     /* a pointer is not aligned to its element size, or
+                                   the workspace is not 256-byte aligned             */
+#define SV_ERR_TOO_LARGE -10    /* the problem exceeds the launch-grid limits        */
+#define SV_ERR_LAUNCH -11       /* the HIP runtime rejected a kernel launch          */
+
+/* Optional outputs for tests and telemetry (every pointer may be NULL;
+ * all are device pointers).  Values for positions the walk did not reach
+ * are NaN. */
+typedef struct {
+    double* p_tok;      /* [B][gamma]   p_i(x_i) for every tested position i       */
+    double* q_tok;      /* [B][gamma]   q_i(x_i) for every tested position i       */
+    double* resid_mass; /* [B]          sum_v max(0, p_n - q_n) when n < gamma     */
+    float*  row_max;    /* [B][gamma+1] max_v z of each row the walk normalised
+                                        (sample) or examined (greedy)            */
+    double* row_sum;    /* [B][gamma+1] sum_v exp((z - row_max) / T), sample mode */
+    /* hipEvent_t handles recorded on `stream` around the two kernel stages:
+     * before the row-statistics stage, between the stages, after the draw
+     * stage.  Any may be NULL. */
+    void* ev_begin;
+    void* ev_mid;
+    void* ev_end;
+} sv_extras_t;
+
+/* Workspace size in bytes for a problem shape (any mode). */
+size_t sv_workspace_bytes(int batch, int gamma, int vocab);
+
+/* Zero-fills `bytes` bytes of a workspace on `stream` with a kernel.  A
+ * workspace must be zero-filled once before its first use; every call of
+ * spec_verify that returns SV_OK leaves it zero-filled again when the
+ * stream has finished the call, for any later problem shape.  After
+ * SV_ERR_LAUNCH, zero-fill it again.  Returns SV_OK or SV_ERR_*. */
+int sv_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * spec_verify -- the batched verify-and-sample step.
+ *
+ *   batch, gamma, vocab   B >= 1, 1 <= gamma <= SV_MAX_GAMMA, V >= 1
+ *   target_logits         [B][gamma+1][V], logits_dtype; finite values or -inf,
+ *                         every row with a finite maximum
+ *   draft_probs           [B][gamma][V], probs_dtype; q >= 0, used as given
+ *                         (not renormalised).  Unused (may be NULL) in greedy mode
+ *   draft_tokens          [B][gamma] int32.  A token outside [0, V) makes the
+ *                         whole sequence invalid: n_accepted[b] = -1 and
+ *                         out_tokens[b][*] = -1
+ *   uniforms              [B][gamma+1] fp32 in (0, 1).  Unused (may be NULL) in
+ *                         greedy mode
+ *   temperature           T > 0, finite, in sample mode; ignored in greedy mode
+ *   mode                  SV_SAMPLE or SV_GREEDY
+ *   n_accepted            [B] int32 out: accepted drafts n in [0, gamma], or -1
+ *   out_tokens            [B][gamma+1] int32 out: x_0..x_{n-1}, t, then -1
+ *   workspace             device buffer of >= sv_workspace_bytes(B, gamma, V)
+ *                         bytes, 256-byte aligned, zero-filled before first use
+ *                         (sv_workspace_init); calls that overlap on the same
+ *                         workspace race
+ *   extras                optional outputs / timing events, or NULL
+ *   stream                hipStream_t to enqueue on
+ *
+ * Returns SV_OK after enqueueing, or a negative SV_ERR_* code without
+ * touching any buffer.  Results are valid once the stream reaches them.
+ */
+int spec_verify(int batch, int gamma, int vocab,
+                const void* target_logits, int logits_dtype,
+                const void* draft_probs, int probs_dtype,
+                const int32_t* draft_tokens, const float* uniforms,
+                float temperature, int mode,
+                int32_t* n_accepted, int32_t* out_tokens,
+                void* workspace, size_t workspace_bytes,
+                const sv_extras_t* extras, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* sv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,182 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded
+inputs, through the C ABI (via the binding).
+
+n_accepted and every output token must be bit-exact, except downstream of a
+decision the oracle flags as near-boundary (uniform within 1e-6 relative of
+an acceptance threshold, within 1e-9 relative of an inverse-CDF boundary);
+flagged decisions are counted and must stay below 1e-4 of all decisions.
+Probabilities at the tested positions match to 1e-6 relative.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from tests import synth
+from tests.gpu_util import check_aux, compare, run_gpu, run_ref
+
+pytestmark = pytest.mark.gpu
+
+_STATS = {"decisions": 0, "flagged_decisions": 0, "sequences": 0, "flagged_sequences": 0}
+
+
+def _check(d, mode="sample", aux=True):
+    print(f"[parity] {d['name']} B={d['B']} gamma={d['gamma']} V={d['V']} mode={mode}", flush=True)
+    g = run_gpu(d, mode, with_aux=aux and mode == "sample")
+    r = run_ref(d, mode)
+    c = compare(g, r, d["gamma"])
+    for k in _STATS:
+        _STATS[k] += c[k]
+    if aux and mode == "sample":
+        check_aux(g, r, 1e-6)
+    return g, r, c
+
+
+# ---------------------------------------------------------- reduced shapes, many seeds
+
+@pytest.mark.parametrize("seed", range(12))
+def test_c2_full_size(seed):
+    _check(synth.make_inputs("c2", seed))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_c3_reduced_ragged(seed):
+    # three 16K-element chunks plus a ragged tail; fp32 draft probs
+    _check(synth.make_inputs("c3", 100 + seed, B=16, V=40_000))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_c4_reduced(seed):
+    _check(synth.make_inputs("c4", 200 + seed, B=32, V=50_000))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_c5_reduced(seed):
+    _check(synth.make_inputs("c5", 300 + seed, B=8, V=70_000))
+
+
+@pytest.mark.parametrize("V", [1, 7, 8, 1001, 20_001])
+def test_unaligned_vocab_scalar_path(V):
+    # V not a multiple of the vector width: scalar loads (bf16 and fp32)
+    _check(synth.make_inputs("c4", 400 + V, B=6, V=V))
+    _check(synth.make_inputs("c2", 500 + V, B=6, V=V))
+
+
+@pytest.mark.parametrize("gamma", [1, 2, 16, 62])
+def test_gamma_extremes(gamma):
+    _check(synth.make_inputs("c4", 600 + gamma, B=4, gamma=gamma, V=3000))
+
+
+def test_greedy_reduced():
+    for seed in range(4):
+        _check(synth.make_inputs("c3", 700 + seed, B=16, V=40_000), mode="greedy")
+
+
+def test_greedy_ties_pick_lowest_index():
+    rng = np.random.default_rng(71)
+    B, gamma, V = 64, 4, 9000
+    z = np.round(rng.standard_normal((B, gamma + 1, V)) * 2).astype(np.float32)  # many exact ties
+    am = np.argmax(z, axis=-1)
+    x = am[:, :gamma].astype(np.int32).copy()
+    x[::3, 2] = (x[::3, 2] + 1) % V
+    d = {"name": "ties", "B": B, "gamma": gamma, "V": V, "temperature": 1.0,
+         "target_logits": synth.f32_to_bf16_bits(z), "draft_tokens": x}
+    g, r, _ = _check(d, mode="greedy", aux=False)
+    assert np.array_equal(g["n_accepted"], r["n_accepted"])
+
+
+def test_c1_trials():
+    d = synth.make_c1(seed=9, trials=100_000)
+    _check(d)
+
+
+# ------------------------------------------------------------------ edge cases
+
+def test_invalid_tokens():
+    d = synth.make_inputs("c4", 801, B=8, V=5000)
+    d["draft_tokens"][1, 3] = 5000
+    d["draft_tokens"][4, 0] = -7
+    d["draft_tokens"][6, 7] = 1 << 30
+    g, r, _ = _check(d)
+    for b in (1, 4, 6):
+        assert g["n_accepted"][b] == -1 and np.all(g["out_tokens"][b] == -1)
+
+
+def test_unused_rows_poisoned_with_nan():
+    d = synth.make_inputs("c2", 802, B=16, V=5000)
+    r0 = run_ref(d)
+    for b, n in enumerate(r0["n_accepted"]):
+        d["target_logits"][b, n + 1:] = np.nan
+        d["draft_probs"][b, n + 1:] = np.nan
+    g = run_gpu(d)
+    assert np.array_equal(g["n_accepted"], r0["n_accepted"])
+    assert np.array_equal(g["out_tokens"], r0["out_tokens"])
+
+
+def test_neg_inf_logits_and_zero_probs():
+    d = synth.make_inputs("c2", 803, B=16, V=4096)
+    rng = np.random.default_rng(803)
+    zl = d["target_logits"]
+    zl[rng.random(zl.shape) < 0.3] = -np.inf
+    zl[:, :, 0] = 0.0  # keep every row's max finite
+    q = d["draft_probs"]
+    q[rng.random(q.shape) < 0.2] = 0.0
+    for b in range(d["B"]):
+        for i in range(d["gamma"]):
+            if q[b, i, d["draft_tokens"][b, i]] == 0:
+                q[b, i, d["draft_tokens"][b, i]] = 1e-3
+    d["draft_probs"][0, 0, d["draft_tokens"][0, 0]] = 0.0  # q(x) = 0 -> accepted
+    _check(d)
+
+
+def test_identical_distributions_take_bonus():
+    B, gamma, V = 32, 5, 4096
+    zl = np.zeros((B, gamma + 1, V), np.float32)
+    q = np.full((B, gamma, V), 1.0 / V, np.float32)
+    rng = np.random.default_rng(804)
+    d = {"name": "same", "B": B, "gamma": gamma, "V": V, "temperature": 1.0,
+         "target_logits": zl, "draft_probs": q,
+         "draft_tokens": rng.integers(0, V, (B, gamma)).astype(np.int32),
+         "uniforms": synth.draw_uniforms(rng, (B, gamma + 1))}
+    g, r, _ = _check(d)
+    assert np.all(g["n_accepted"] == gamma)
+
+
+def test_zero_residual_fallback():
+    # q >= p everywhere: a rejection leaves no residual mass -> draw from p
+    B, gamma, V = 64, 2, 3000
+    rng = np.random.default_rng(805)
+    z = rng.standard_normal((gamma + 1, V)).astype(np.float32)
+    p = np.exp(z.astype(np.float64) - z.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    q = (p[:gamma] * 1.5 + 1e-4).astype(np.float32)
+    d = {"name": "fallback", "B": B, "gamma": gamma, "V": V, "temperature": 1.0,
+         "target_logits": np.ascontiguousarray(np.broadcast_to(z, (B, gamma + 1, V))),
+         "draft_probs": np.ascontiguousarray(np.broadcast_to(q, (B, gamma, V))),
+         "draft_tokens": rng.integers(0, V, (B, gamma)).astype(np.int32),
+         "uniforms": synth.draw_uniforms(rng, (B, gamma + 1))}
+    g, r, _ = _check(d)
+    assert np.any(r["n_accepted"] < gamma)
+
+
+def test_repeated_calls_reuse_workspace():
+    # the control region must be left clean: alternate shapes and modes
+    import torch
+    shapes = [("c4", dict(B=8, V=30_000)), ("c2", dict(B=3, V=500)), ("c5", dict(B=2, V=40_000))]
+    import exact_rejection_sampling_temp_amd as sv
+    for rep in range(2):
+        for name, kw in shapes:
+            d = synth.make_inputs(name, 900 + rep, **kw)
+            _check(d)
+            _check(d, mode="greedy", aux=False)
+            torch.cuda.synchronize()
+            for ws in sv._ws_cache.values():
+                assert int(ws.count_nonzero()) == 0, "a finished call must leave the workspace zero"
+
+
+def test_zz_report_flag_rate():
+    s = _STATS
+    print(f"[parity] totals {json.dumps(s)}", flush=True)
+    if s["decisions"]:
+        assert s["flagged_decisions"] / s["decisions"] < 1e-4
