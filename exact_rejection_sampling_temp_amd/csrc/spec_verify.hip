@@ -11,7 +11,7 @@
 //   [ST] "The exact decoding shortcut that burns compute when guesses miss":
 //        correction_distribution (target row when the residual mass <= 1e-15).
 //
-// Two launches per call, both on the caller's stream:
+// Three launches per call (two in greedy mode), all on the caller's stream:
 //
 //   1. row stage (k_rows_sample / k_rows_greedy).  The grid enumerates
 //      (position k, sequence b, chunk c) with k slowest.  A workgroup streams
@@ -26,14 +26,14 @@
 //      order most of them are never read.  The decision at each position is
 //      independent of the others, so skipping changes no result.
 //
-//   2. draw stage (k_draw_sample / k_draw_greedy).  n is the index of the
-//      lowest set bit of the reject mask (gamma if none).  For every sequence
-//      the row n of the target (and of the draft, when n < gamma) is
-//      streamed in chunks; each workgroup computes, in double precision,
-//      e_v = exp((z_v - max)/T) and the chunk sums needed for the residual
-//      mass; the last workgroup of the sequence turns them into the exact
-//      row normaliser, picks the chunk holding the inverse-CDF target and
-//      scans it to find the token.
+//   2. draw stage (k_draw_sums + k_draw_finish, or k_draw_greedy).  n is the
+//      index of the lowest set bit of the reject mask (gamma if none).  For
+//      every sequence the row n of the target (and of the draft, when
+//      n < gamma) is streamed in chunks; each workgroup computes, in double
+//      precision, e_v = exp((z_v - max)/T) and the chunk sums needed for the
+//      residual mass.  Then one workgroup per sequence turns them into the
+//      exact row normaliser, picks the chunk holding the inverse-CDF target
+//      and scans it to find the token.
 //
 // Numerics.  The row stage uses fp32 exp2 with a two-term log2(e)/T and a
 // per-chunk correction of the rounded shift, and accumulates in fp64; the
@@ -68,8 +68,8 @@ constexpr int kEptBf16 = 64;
 constexpr int kEptFp32 = 32;
 constexpr int kChunkBf16 = kEptBf16 * kThreads;  // 16384 elements
 constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
-// Elements per thread of one draw-stage chunk (a chunk is 4096 elements).
-constexpr int kEpt2 = 16;
+// Elements per thread of one draw-stage chunk (a chunk is 8192 elements).
+constexpr int kEpt2 = 32;
 constexpr int kChunk2 = kEpt2 * kThreads;
 
 // Per-row statistics written by the row stage, read by the draw stage.
@@ -84,16 +84,15 @@ static_assert(sizeof(RowStat) == 32, "RowStat layout");
 
 // Per-chunk partial of the draw stage.
 struct DrawPart {
-    double E;      // sum of e_v over the chunk
-    double EA;     // sum of e_v over {v : p_v > q_v} (residual support)
-    double QA;     // sum of q_v over the same set
-    int32_t lastA; // largest index in the residual support, -1 if none
-    int32_t lastE; // largest index with e_v > 0, -1 if none
+    double E;   // sum of e_v over the chunk
+    double EA;  // sum of e_v over {v : p_v > q_v} (residual support)
+    double QA;  // sum of q_v over the same set
+    double pad;
 };
 static_assert(sizeof(DrawPart) == 32, "DrawPart layout");
 
 struct Layout {
-    size_t mask_off, cnt1_off, cnt2_off, control_bytes;
+    size_t mask_off, cnt1_off, control_bytes;
     size_t part1_off, stats_off, part2_off, total;
     int nch1_max, nch2_max;
 };
@@ -109,7 +108,6 @@ Layout make_layout(int B, int gamma, int V)
     size_t off = 0;
     L.mask_off = off;  off = align256(off + sizeof(uint64_t) * (size_t)B);
     L.cnt1_off = off;  off = align256(off + sizeof(uint32_t) * rows);
-    L.cnt2_off = off;  off = align256(off + sizeof(uint32_t) * (size_t)B);
     L.control_bytes = off;
     L.part1_off = off; off = align256(off + 2 * sizeof(uint64_t) * rows * (size_t)L.nch1_max);
     L.stats_off = off; off = align256(off + sizeof(RowStat) * rows);
@@ -382,35 +380,22 @@ __device__ __forceinline__ bool chunk_skipped(const RowParams& p, int b, int k, 
 }
 
 // Shared epilogue: count this block in and learn whether it is the last
-// block of the row (returns 0: not last, 1: last and every chunk was done,
-// 2: last but some chunk was skipped).  The counter keeps arrivals in its low
-// 16 bits and skips in its high bits; the last block resets it to zero.
-__device__ __forceinline__ int row_arrive(const RowParams& p, int64_t row, bool skip, uint32_t dep, int* sm_flag)
+// block of the row; the last block resets the counter to zero.  Blocks that
+// skip their chunk never count in, so a row with a skipped chunk has no last
+// block (it is not needed: an earlier position was rejected); the draw stage
+// clears such a row's counter and partial slots.
+__device__ __forceinline__ bool row_arrive(const RowParams& p, int64_t row, uint32_t dep, int* sm_flag)
 {
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t inc = (skip ? 0x10001u : 1u) + dep;
-        const uint32_t old = __hip_atomic_fetch_add(&p.cnt1[row], inc, __ATOMIC_RELAXED,
+        const uint32_t old = __hip_atomic_fetch_add(&p.cnt1[row], 1u + dep, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = (old & 0xffffu) + 1u == (uint32_t)p.nch;
-        const bool any_skip = skip || (old >> 16) != 0u;
+        const bool last = old + 1u == (uint32_t)p.nch;
         if (last) __hip_atomic_store(&p.cnt1[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *sm_flag = last ? (any_skip ? 2 : 1) : 0;
+        *sm_flag = last ? 1 : 0;
     }
     __syncthreads();
-    return *sm_flag;
-}
-
-// The last block of a row clears the row's partial slots once it has read
-// them, so that a finished call leaves the whole workspace zero (a later
-// call with another shape may place its counters there).
-__device__ __forceinline__ void clear_row_partials(const RowParams& p, int64_t row)
-{
-    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
-        uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
-        st_agent(slot, 0ull);
-        st_agent(slot + 1, 0ull);
-    }
+    return *sm_flag != 0;
 }
 
 // ----------------------------------------------------------------- row stage, sample
@@ -431,9 +416,9 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
     __shared__ double sm_d[kWaves];
     __shared__ int sm_flag;
 
-    const bool skip = chunk_skipped(p, b, k, &sm_flag);
+    if (chunk_skipped(p, b, k, &sm_flag)) return;
     uint32_t dep = 0;
-    if (!skip) {
+    {
         const int v0 = c * CH;
         const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
         float x[EPT];
@@ -472,12 +457,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         }
     }
 
-    const int arrival = row_arrive(p, row, skip, dep, &sm_flag);
-    if (arrival == 0) return;
-    if (arrival == 2) {  // row not needed: an earlier position was rejected
-        clear_row_partials(p, row);
-        return;
-    }
+    if (!row_arrive(p, row, dep, &sm_flag)) return;
 
     // Last block of a fully processed row: merge the chunk partials.
     float M = -INFINITY;
@@ -493,8 +473,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         const double sj = __longlong_as_double((long long)ld_agent(slot + 1));
         if (mj > -INFINITY) S += sj * exp2(((double)mj - (double)M) * p.cd);
     }
-    S = block_sum(S, sm_d);  // (its barriers end every read of the slots)
-    clear_row_partials(p, row);
+    S = block_sum(S, sm_d);
 
     if (threadIdx.x == 0) {
         RowStat st;
@@ -546,9 +525,9 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
     __shared__ int sm_i[kWaves];
     __shared__ int sm_flag;
 
-    const bool skip = chunk_skipped(p, b, k, &sm_flag);
+    if (chunk_skipped(p, b, k, &sm_flag)) return;
     uint32_t dep = 0;
-    if (!skip) {
+    {
         const int v0 = c * CH;
         const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
         float x[EPT];
@@ -567,12 +546,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
         }
     }
 
-    const int arrival = row_arrive(p, row, skip, dep, &sm_flag);
-    if (arrival == 0) return;
-    if (arrival == 2) {
-        clear_row_partials(p, row);
-        return;
-    }
+    if (!row_arrive(p, row, dep, &sm_flag)) return;
 
     float bv = -INFINITY;
     int bi = INT_MAX;
@@ -581,7 +555,6 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
         amax_merge(bv, bi, __uint_as_float((uint32_t)w), (int)(uint32_t)(w >> 32));
     }
     block_amax(bv, bi, sm_f, sm_i);
-    clear_row_partials(p, row);
     if (threadIdx.x == 0) {
         RowStat st;
         st.m = bv;
@@ -610,7 +583,9 @@ struct DrawParams {
     const int32_t* tokens;
     const float* uniforms;
     uint64_t* mask;
-    uint32_t* cnt2;
+    uint32_t* cnt1;   // row-stage counters and partial slots, cleared per sequence
+    uint64_t* part1;
+    int nch1;
     RowStat* stats;
     DrawPart* part2;  // [B][nch2]
     int32_t* n_out;
@@ -625,19 +600,41 @@ struct DrawParams {
     double cd;
 };
 
-// Writes the per-sequence outputs and telemetry, and clears the sequence's
-// reject mask for the next call.  Called by the whole block.
-__device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool invalid, double Z, bool sample)
+// Per-position values the finish of a sequence needs, loaded early by thread
+// i (= position i <= gamma; gamma + 1 <= kThreads): the draft token x_i and
+// the statistics of row i.
+struct PosInfo {
+    int32_t tok;
+    RowStat st;
+};
+__device__ __forceinline__ PosInfo load_pos_info(const DrawParams& p, int b)
+{
+    PosInfo pi;
+    pi.tok = 0;
+    pi.st = RowStat{0.0f, 0, 0.0, 0.0, 0.0};
+    const int i = threadIdx.x;
+    if (i <= p.gamma) {
+        pi.st = p.stats[(int64_t)b * (p.gamma + 1) + i];
+        if (i < p.gamma) pi.tok = p.tokens[(int64_t)b * p.gamma + i];
+    }
+    return pi;
+}
+
+// Writes the per-sequence outputs and telemetry, and clears what the call
+// left in the workspace for this sequence.  Called by the whole block.
+__device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool invalid, double Z, bool sample,
+                                const PosInfo& pi)
 {
     const int G1 = p.gamma + 1;
-    for (int i = threadIdx.x; i < G1; i += kThreads) {
+    const int i = threadIdx.x;
+    if (i < G1) {
         int32_t o;
         if (invalid) o = -1;
-        else if (i < n) o = p.tokens[(int64_t)b * p.gamma + i];
+        else if (i < n) o = pi.tok;
         else if (i == n) o = t;
         else o = -1;
         p.tok_out[(int64_t)b * G1 + i] = o;
-        const RowStat st = p.stats[(int64_t)b * G1 + i];
+        const RowStat& st = pi.st;
         p.stats[(int64_t)b * G1 + i] = RowStat{0.0f, 0, 0.0, 0.0, 0.0};  // leave the workspace zero
         const bool row_seen = !invalid && i <= n;
         if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + i] = row_seen ? st.m : NAN;
@@ -648,6 +645,15 @@ __device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool i
             if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + i] = tested ? st.Q : NAN;
         }
     }
+    // rows whose chunks were partly skipped kept their arrival count and
+    // partials: clear every row-stage slot of this sequence
+    for (int j = threadIdx.x; j < G1 * p.nch1; j += kThreads) {
+        uint64_t* slot = p.part1 + 2 * ((size_t)b * G1 * p.nch1 + j);
+        st_agent(slot, 0ull);
+        st_agent(slot + 1, 0ull);
+    }
+    for (int i = threadIdx.x; i < G1; i += kThreads)
+        __hip_atomic_store(&p.cnt1[(int64_t)b * G1 + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) {
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = (!invalid && sample && n < p.gamma) ? Z : NAN;
@@ -657,43 +663,43 @@ __device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool i
 
 __device__ __forceinline__ void clear_draw_partials(const DrawParams& p, int b)
 {
-    for (int j = threadIdx.x; j < p.nch2; j += kThreads) {
-        uint64_t* slot = reinterpret_cast<uint64_t*>(p.part2 + (size_t)b * p.nch2 + j);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) st_agent(slot + w, 0ull);
-    }
+    for (int j = threadIdx.x; j < p.nch2; j += kThreads) p.part2[(size_t)b * p.nch2 + j] = DrawPart{0.0, 0.0, 0.0, 0.0};
 }
 
 // Any draft token of sequence b outside [0, V)?  (Checked over all gamma
-// tokens, also those past the first rejection.)
-__device__ bool tokens_invalid(const DrawParams& p, int b, int* sm_i)
+// tokens, also those past the first rejection.)  Called by the whole block.
+__device__ bool tokens_invalid(const DrawParams& p, const PosInfo& pi, int* sm_i)
 {
-    int bad = 0;
-    for (int i = threadIdx.x; i < p.gamma; i += kThreads) {
-        const int x = p.tokens[(int64_t)b * p.gamma + i];
-        bad |= (x < 0 || x >= p.V) ? 1 : 0;
-    }
+    const int i = threadIdx.x;
+    const int bad = (i < p.gamma && (pi.tok < 0 || pi.tok >= p.V)) ? 1 : 0;
     return block_max_i(bad, sm_i) != 0;
 }
 
-// 2^a in double for any a <= 0 (including -inf), accurate to a few ulp:
-// a = (k + f) / 64 with k integer and |f| <= 1/2, 2^a = 2^(k >> 6) *
-// 2^((k & 63)/64) * exp(f ln2 / 64); the middle factor comes from a 64-entry
-// table in LDS and the last from its degree-5 Taylor polynomial (remainder
-// below 4e-17).
-__device__ __forceinline__ double exp2_tab(double a, const double* tab)
+// 2^a in double for a <= 0, relative error below 2e-14: a = k + f with k
+// the nearest integer (rounded by adding 1.5 * 2^52, which leaves k in the
+// low word) and |f| <= 1/2; 2^f by a degree-9 polynomial interpolating it at
+// Chebyshev nodes of [-1/2, 1/2]; 2^k is added to the exponent field.  Below
+// -1020 (and for -inf or NaN) the result is 0.
+__device__ __forceinline__ double exp2_f64(double a)
 {
-    a = fmax(a, -1100.0);  // -inf and huge negatives: the ldexp underflows to 0
-    const double t = a * 64.0;
-    const double kf = rint(t);
-    const double r = (t - kf) * 0.010830424696249145;  // ln(2) / 64
-    const int k = (int)kf;
-    double poly = fma(r, 1.0 / 120.0, 1.0 / 24.0);
-    poly = fma(r, poly, 1.0 / 6.0);
-    poly = fma(r, poly, 0.5);
-    poly = fma(r, poly, 1.0);
-    poly = fma(r, poly, 1.0);
-    return ldexp(tab[k & 63] * poly, k >> 6);
+    const bool tiny = !(a >= -1020.0);
+    a = tiny ? -1020.0 : a;
+    const double magic = 6755399441055744.0;
+    const double t = a + magic;
+    const double f = a - (t - magic);
+    const int k = __double2loint(t);
+    double p = 1.0208789509527192e-07;
+    p = fma(f, p, 1.3259656070717964e-06);
+    p = fma(f, p, 1.5252656913569549e-05);
+    p = fma(f, p, 0.00015403433688494325);
+    p = fma(f, p, 0.0013333558230514875);
+    p = fma(f, p, 0.009618129194063072);
+    p = fma(f, p, 0.05550410866444786);
+    p = fma(f, p, 0.24022650695639422);
+    p = fma(f, p, 0.6931471805599502);
+    p = fma(f, p, 1.0000000000000138);
+    const double r = __hiloint2double(__double2hiint(p) + (int)((unsigned)k << 20), __double2loint(p));
+    return tiny ? 0.0 : r;
 }
 
 // Loads 8 consecutive elements starting at idx (a multiple of 8 on the
@@ -737,149 +743,255 @@ __device__ __forceinline__ void load8(const void* rowp, int idx, int V, float pa
     }
 }
 
-// Chunk sums of the draw stage for this thread's 16 elements: groups of 8
-// consecutive elements at v0 + (g * kThreads + tid) * 8, g = 0, 1.
+// 8 consecutive elements as raw 128-bit words (one for bf16, two for fp32).
+struct Raw8 {
+    uint4 a, b;
+};
+template <int DT, bool FULL>
+__device__ __forceinline__ Raw8 load_raw8(const void* rowp, int idx, int V)
+{
+    constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
+    const int ci = FULL ? idx : min(idx, V - 8);
+    const char* ptr = static_cast<const char*>(rowp) + (size_t)ci * ES;
+    Raw8 r;
+    r.a = *reinterpret_cast<const uint4*>(ptr);
+    if constexpr (DT == SV_FP32) r.b = *reinterpret_cast<const uint4*>(ptr + 16);
+    else r.b = make_uint4(0u, 0u, 0u, 0u);
+    return r;
+}
+template <int DT>
+__device__ __forceinline__ float raw8_elem(const Raw8& r, int e)
+{
+    if constexpr (DT == SV_BF16) {
+        const uint32_t w = e < 2 ? r.a.x : e < 4 ? r.a.y : e < 6 ? r.a.z : r.a.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+        const uint32_t w = e == 0 ? r.a.x : e == 1 ? r.a.y : e == 2 ? r.a.z : e == 3 ? r.a.w
+                         : e == 4 ? r.b.x : e == 5 ? r.b.y : e == 6 ? r.b.z : r.b.w;
+        return __uint_as_float(w);
+    }
+}
+
+// Chunk sums of the draw stage for this thread's kEpt2 elements: groups of 8
+// consecutive elements at v0 + (g * kThreads + tid) * 8.  Every load of the
+// chunk is issued before the arithmetic starts.
 template <int DT, int PT, bool VEC, bool FULL>
 __device__ __forceinline__ void draw_chunk_sums(const DrawParams& p, const void* zrow, const void* qrow,
-                                                bool resid, int v0, double M, double S_row,
-                                                const double* tab, double& E, double& EA, double& QA,
-                                                int& lastA, int& lastE)
+                                                bool resid, int v0, double nMcd, double S_row,
+                                                double& E, double& EA, double& QA)
 {
-    float z[kEpt2], q[kEpt2];
-#pragma unroll
-    for (int g = 0; g < kEpt2 / 8; ++g)
-        load8<DT, VEC, FULL>(zrow, v0 + (g * kThreads + (int)threadIdx.x) * 8, p.V, -INFINITY, z + g * 8);
-    if (resid) {
-#pragma unroll
-        for (int g = 0; g < kEpt2 / 8; ++g)
-            load8<PT, VEC, FULL>(qrow, v0 + (g * kThreads + (int)threadIdx.x) * 8, p.V, 0.0f, q + g * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < kEpt2; ++i) {
-        const int v = v0 + ((i / 8) * kThreads + (int)threadIdx.x) * 8 + (i % 8);
-        const double e = exp2_tab(((double)z[i] - M) * p.cd, tab);
+    constexpr int NG = kEpt2 / 8;
+    const int tid = (int)threadIdx.x;
+    // e_v = 2^((z - M) log2(e)/T); the shift -M log2(e)/T is rounded once for
+    // the whole row, a common factor that cancels in every ratio used
+    auto element = [&](float zf, float qf) {
+        const double e = exp2_f64(fma((double)zf, p.cd, nMcd));
         E += e;
-        if (e > 0.0) lastE = v;
         if (resid) {
-            const double qd = (double)q[i];
-            if (e > qd * S_row) { EA += e; QA += qd; lastA = v; }
+            const double qd = (double)qf;
+            if (e > qd * S_row) { EA += e; QA += qd; }
+        }
+    };
+    if constexpr (VEC) {
+        Raw8 zr[NG], qr[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) zr[g] = load_raw8<DT, FULL>(zrow, v0 + (g * kThreads + tid) * 8, p.V);
+        if (resid) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) qr[g] = load_raw8<PT, FULL>(qrow, v0 + (g * kThreads + tid) * 8, p.V);
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int idx = v0 + (g * kThreads + tid) * 8;
+            if (!FULL && idx >= p.V) continue;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) element(raw8_elem<DT>(zr[g], e), resid ? raw8_elem<PT>(qr[g], e) : 0.0f);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const int idx = v0 + (g * kThreads + tid) * 8;
+            float z[8], q[8];
+            load8<DT, false, FULL>(zrow, idx, p.V, -INFINITY, z);
+            if (resid) load8<PT, false, FULL>(qrow, idx, p.V, 0.0f, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (FULL || idx + e < p.V) element(z[e], resid ? q[e] : 0.0f);
         }
     }
 }
 
-// The weights of one thread's contiguous run of 16 elements, [v0, v0 + 16),
-// for the inverse-CDF scan: max(0, p_v - q_v) or e_v.
-template <int DT, int PT, bool VEC, bool FULL>
-__device__ __forceinline__ void draw_run_weights(const DrawParams& p, const void* zrow, const void* qrow,
-                                                 bool use_resid, int v0, double M, double S,
-                                                 const double* tab, double (&w)[kEpt2])
+// Weight of one element of row n for the inverse-CDF draw: max(0, p - q)
+// with p = e / S, or e itself for the bonus / fallback draw.
+__device__ __forceinline__ double draw_weight(const DrawParams& p, bool use_resid, float z, float q, double nMcd,
+                                              double invS)
 {
-    float z[kEpt2], q[kEpt2];
-#pragma unroll
-    for (int g = 0; g < kEpt2 / 8; ++g) load8<DT, VEC, FULL>(zrow, v0 + g * 8, p.V, -INFINITY, z + g * 8);
-    if (use_resid) {
-#pragma unroll
-        for (int g = 0; g < kEpt2 / 8; ++g) load8<PT, VEC, FULL>(qrow, v0 + g * 8, p.V, 0.0f, q + g * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < kEpt2; ++i) {
-        const double e = exp2_tab(((double)z[i] - M) * p.cd, tab);
-        w[i] = use_resid ? fmax(0.0, e / S - (double)q[i]) : e;
-        if (v0 + i >= p.V) w[i] = 0.0;
-    }
+    const double e = exp2_f64(fma((double)z, p.cd, nMcd));
+    return use_resid ? fmax(0.0, e * invS - (double)q) : e;
 }
 
-__device__ __forceinline__ const uint64_t* draw_slot(const DrawParams& p, int b, int j)
-{
-    return reinterpret_cast<const uint64_t*>(p.part2 + (size_t)b * p.nch2 + j);
-}
-__device__ __forceinline__ double slot_d(const uint64_t* s, int w)
-{
-    return __longlong_as_double((long long)ld_agent(s + w));
-}
-
+// This thread's share of one draw-stage chunk of row n (and of the draft
+// row): group g holds the 8 elements from base + (g * kThreads + tid) * 8.
+// Vector path: raw 128-bit words, all loads issued together; otherwise
+// unpacked floats.  Elements past V must be ignored by the caller.
 template <int DT, int PT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw_sample(const DrawParams p)
+struct ChunkBuf {
+    static constexpr int NG = kEpt2 / 8;
+    Raw8 zr[NG], qr[NG];
+    __device__ __forceinline__ void load(const DrawParams& p, const void* zrow, const void* qrow, bool with_q, int base)
+    {
+        const int tid = (int)threadIdx.x;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) zr[g] = load_raw8<DT, false>(zrow, base + (g * kThreads + tid) * 8, p.V);
+        if (with_q) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) qr[g] = load_raw8<PT, false>(qrow, base + (g * kThreads + tid) * 8, p.V);
+        }
+    }
+    __device__ __forceinline__ float z(int g, int e) const { return raw8_elem<DT>(zr[g], e); }
+    __device__ __forceinline__ float q(int g, int e) const { return raw8_elem<PT>(qr[g], e); }
+};
+template <int DT, int PT>
+struct ChunkBuf<DT, PT, false> {
+    static constexpr int NG = kEpt2 / 8;
+    float zv[NG][8], qv[NG][8];
+    __device__ __forceinline__ void load(const DrawParams& p, const void* zrow, const void* qrow, bool with_q, int base)
+    {
+        const int tid = (int)threadIdx.x;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = min(base + (g * kThreads + tid) * 8 + e, p.V - 1);
+                zv[g][e] = load_one<DT>(zrow, i);
+                qv[g][e] = with_q ? load_one<PT>(qrow, i) : 0.0f;
+            }
+    }
+    __device__ __forceinline__ float z(int g, int e) const { return zv[g][e]; }
+    __device__ __forceinline__ float q(int g, int e) const { return qv[g][e]; }
+};
+
+// Where the draw of sequence b reads: n from the reject mask, row n of the
+// target (and of the draft when n < gamma), and the row stage's statistics.
+struct SeqDraw {
+    int n;
+    bool resid;         // n < gamma: residual draw, else bonus draw
+    bool invalid_seen;  // the row stage met an out-of-range draft token
+    const void* zrow;
+    const void* qrow;
+    double nMcd;        // -max_v z * log2(e)/T, rounded once for the row
+    double S_row;       // the row stage's normaliser (fp32 exponentials)
+};
+template <int DT, int PT>
+__device__ __forceinline__ SeqDraw seq_draw(const DrawParams& p, int b)
+{
+    SeqDraw sd;
+    const uint64_t m = p.mask[b];
+    const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
+    sd.invalid_seen = (m & kInvalidBit) != 0;
+    sd.n = rej ? __builtin_ctzll(rej) : p.gamma;
+    sd.resid = sd.n < p.gamma;
+    const int64_t row = (int64_t)b * (p.gamma + 1) + sd.n;
+    const RowStat st = p.stats[row];  // in bounds for any mask (n <= gamma)
+    sd.nMcd = -(double)st.m * p.cd;
+    sd.S_row = st.S;
+    sd.zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+    sd.qrow = sd.resid ? static_cast<const char*>(p.probs) +
+                             (size_t)((int64_t)b * p.gamma + sd.n) * p.V * (PT == SV_BF16 ? 2 : 4)
+                       : nullptr;
+    return sd;
+}
+
+// Draw stage, first kernel: the chunk sums of row n, one block per (sequence,
+// chunk).  They are consumed by the next kernel, so plain stores suffice.
+template <int DT, int PT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draw_sums(const DrawParams p)
 {
     const int b = (int)(blockIdx.x / (unsigned)p.nch2);
     const int c = (int)(blockIdx.x % (unsigned)p.nch2);
-    const int G1 = p.gamma + 1;
+    __shared__ double sm_d[kWaves];
+    const SeqDraw sd = seq_draw<DT, PT>(p, b);
+    if (sd.invalid_seen) return;
+    double E = 0.0, EA = 0.0, QA = 0.0;
+    const int v0 = c * kChunk2;
+    // S_row (row stage) only decides which elements lie in the residual
+    // support; the normaliser itself is re-summed in fp64 here.
+    if (v0 + kChunk2 <= p.V)
+        draw_chunk_sums<DT, PT, VEC, true>(p, sd.zrow, sd.qrow, sd.resid, v0, sd.nMcd, sd.S_row, E, EA, QA);
+    else
+        draw_chunk_sums<DT, PT, VEC, false>(p, sd.zrow, sd.qrow, sd.resid, v0, sd.nMcd, sd.S_row, E, EA, QA);
+    E = block_sum(E, sm_d);
+    EA = block_sum(EA, sm_d);
+    QA = block_sum(QA, sm_d);
+    if (threadIdx.x == 0) {
+        DrawPart* slot = p.part2 + (size_t)b * p.nch2 + c;
+        slot->E = E;
+        slot->EA = EA;
+        slot->QA = QA;
+    }
+}
 
-    __shared__ double tab[64];
+// Draw stage, second kernel: one block per sequence turns the chunk sums into
+// the exact normaliser and residual mass, finds the chunk that holds the
+// inverse-CDF target, scans it for the token and writes the outputs.  (A
+// separate launch spreads these blocks evenly over the XCDs; run by whichever
+// block of a sequence finished last, they piled up on one XCD.)
+template <int DT, int PT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draw_finish(const DrawParams p)
+{
+    const int b = blockIdx.x;
+    const int G1 = p.gamma + 1;
     __shared__ double sm_d[kWaves];
     __shared__ int sm_i[kWaves];
-    __shared__ int sm_flag;
     __shared__ double sm_pre;
+    const SeqDraw sd = seq_draw<DT, PT>(p, b);
+    const int n = sd.n;
+    const bool resid = sd.resid;
+    const bool invalid_seen = sd.invalid_seen;
+    const void* zrow = sd.zrow;
+    const void* qrow = sd.qrow;
+    const double nMcd = sd.nMcd;
 
-    if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
-
-    const uint64_t m = p.mask[b];
-    const bool invalid_seen = (m & kInvalidBit) != 0;
-    const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
-    const int n = rej ? __builtin_ctzll(rej) : p.gamma;
-    const bool resid = n < p.gamma;
-    const int64_t row = (int64_t)b * G1 + n;
-    const int64_t qrow_i = (int64_t)b * p.gamma + n;
-    const RowStat st = p.stats[row];  // in bounds for any mask (n <= gamma)
-    const double M = (double)st.m;
-    const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
-    const void* qrow = resid ? static_cast<const char*>(p.probs) + (size_t)qrow_i * p.V * (PT == SV_BF16 ? 2 : 4)
-                             : nullptr;
-    __syncthreads();  // table ready
-
-    uint32_t dep = 0;
-    if (!invalid_seen) {
-        double E = 0.0, EA = 0.0, QA = 0.0;
-        int lastA = -1, lastE = -1;
-        const int v0 = c * kChunk2;
-        // st.S (row stage) only decides which elements lie in the residual
-        // support; the normaliser itself is re-summed in fp64 below.
-        if (v0 + kChunk2 <= p.V)
-            draw_chunk_sums<DT, PT, VEC, true>(p, zrow, qrow, resid, v0, M, st.S, tab, E, EA, QA, lastA, lastE);
-        else
-            draw_chunk_sums<DT, PT, VEC, false>(p, zrow, qrow, resid, v0, M, st.S, tab, E, EA, QA, lastA, lastE);
-        E = block_sum(E, sm_d);
-        EA = block_sum(EA, sm_d);
-        QA = block_sum(QA, sm_d);
-        lastA = block_max_i(lastA, sm_i);
-        lastE = block_max_i(lastE, sm_i);
-        if (threadIdx.x == 0) {
-            const uint64_t w[4] = {(uint64_t)__double_as_longlong(E), (uint64_t)__double_as_longlong(EA),
-                                   (uint64_t)__double_as_longlong(QA),
-                                   ((uint64_t)(uint32_t)lastE << 32) | (uint64_t)(uint32_t)lastA};
-            dep = publish(reinterpret_cast<uint64_t*>(p.part2 + (size_t)b * p.nch2 + c), w, p.zero);
-        }
+    // One round trip brings everything the finish needs: the chunk sums
+    // (slot j cached by thread j), the uniform of the draw, and the draft
+    // tokens and row statistics of the outputs.
+    const int tid = (int)threadIdx.x;
+    const PosInfo pi = load_pos_info(p, b);
+    const double ug = (double)p.uniforms[(int64_t)b * G1 + p.gamma];
+    const DrawPart* slots = p.part2 + (size_t)b * p.nch2;
+    double cE = 0.0, cEA = 0.0, cQA = 0.0;
+    if (tid < p.nch2) {
+        cE = slots[tid].E;
+        cEA = slots[tid].EA;
+        cQA = slots[tid].QA;
     }
+    auto slot3 = [&](int j, double& E, double& EA, double& QA) {
+        if (j == tid) { E = cE; EA = cEA; QA = cQA; return; }
+        E = slots[j].E; EA = slots[j].EA; QA = slots[j].QA;
+    };
 
-    // arrival count; the last block of the sequence finishes it
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&p.cnt2[b], 1u + dep, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old + 1u == (uint32_t)p.nch2;
-        if (last) __hip_atomic_store(&p.cnt2[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_flag = last ? 1 : 0;
-    }
-    __syncthreads();
-    if (sm_flag == 0) return;
-
-    const bool bad_token = tokens_invalid(p, b, sm_i);  // called by every thread (barriers)
+    const bool bad_token = tokens_invalid(p, pi, sm_i);  // called by every thread (barriers)
     const bool invalid = invalid_seen || bad_token;
     if (invalid) {
         clear_draw_partials(p, b);
-        finish_sequence(p, b, n, -1, true, NAN, true);
+        finish_sequence(p, b, n, -1, true, NAN, true, pi);
         return;
     }
 
     // exact normaliser of row n and the residual mass, from the chunk sums
     double S = 0.0;
-    for (int j = threadIdx.x; j < p.nch2; j += kThreads) S += slot_d(draw_slot(p, b, j), 0);
+    for (int j = tid; j < p.nch2; j += kThreads) {
+        double E, EA, QA;
+        slot3(j, E, EA, QA);
+        S += E;
+    }
     S = block_sum(S, sm_d);
     double Z = 0.0;
     if (resid) {
-        for (int j = threadIdx.x; j < p.nch2; j += kThreads) {
-            const uint64_t* sl = draw_slot(p, b, j);
-            Z += fmax(0.0, slot_d(sl, 1) / S - slot_d(sl, 2));
+        for (int j = tid; j < p.nch2; j += kThreads) {
+            double E, EA, QA;
+            slot3(j, E, EA, QA);
+            Z += fmax(0.0, EA / S - QA);
         }
         Z = block_sum(Z, sm_d);
     }
@@ -887,19 +999,21 @@ __global__ __launch_bounds__(kThreads) void k_draw_sample(const DrawParams p)
     // [ST]'s fallback to p_n; the bonus row p_gamma after full acceptance.
     const bool use_resid = resid && Z > kResidEps;
     const double total = use_resid ? Z : S;
-    const double target = (double)p.uniforms[(int64_t)b * G1 + p.gamma] * total;
+    const double invS = 1.0 / S;  // p_v = e_v * invS (within an ulp of e_v / S)
+    const double target = ug * total;
+    auto chunk_weight = [&](int j) {
+        double E, EA, QA;
+        slot3(j, E, EA, QA);
+        return use_resid ? fmax(0.0, EA / S - QA) : E;
+    };
 
     // the first chunk whose running weight sum exceeds the target (block scan
-    // over the chunk weights, 256 chunks per round)
+    // over the chunk weights, kThreads chunks per round)
     int jc = -1;
     double carry = 0.0;
     for (int j0 = 0; j0 < p.nch2 && jc < 0; j0 += kThreads) {
-        const int j = j0 + (int)threadIdx.x;
-        double w = 0.0;
-        if (j < p.nch2) {
-            const uint64_t* sl = draw_slot(p, b, j);
-            w = use_resid ? fmax(0.0, slot_d(sl, 1) / S - slot_d(sl, 2)) : slot_d(sl, 0);
-        }
+        const int j = j0 + tid;
+        const double w = j < p.nch2 ? chunk_weight(j) : 0.0;
         double tot;
         const double excl = block_exclusive_scan(w, sm_d, &tot);
         const bool hit = j < p.nch2 && w > 0.0 && carry + excl + w > target;
@@ -917,46 +1031,70 @@ __global__ __launch_bounds__(kThreads) void k_draw_sample(const DrawParams p)
     double rem = target - carry;  // target relative to the start of chunk jc
 
     // scan chunk jc (and, only if rounding pushed the crossing out of it, the
-    // chunks after it): thread t owns the contiguous run [16 t, 16 t + 16)
+    // chunks after it) in index order: group g of thread t holds the 8
+    // elements from jc * kChunk2 + (g * kThreads + t) * 8, so the groups are
+    // visited g-major and, within a group, by thread.  The chunk's loads are
+    // all issued before the first group is scanned.
     int tok = -1;
     while (jc >= 0 && jc < p.nch2 && tok < 0) {
-        const int base = jc * kChunk2 + (int)threadIdx.x * kEpt2;
-        double w[kEpt2];
-        if (jc * kChunk2 + kChunk2 <= p.V)
-            draw_run_weights<DT, PT, VEC, true>(p, zrow, qrow, use_resid, base, M, S, tab, w);
-        else
-            draw_run_weights<DT, PT, VEC, false>(p, zrow, qrow, use_resid, base, M, S, tab, w);
-        double local = 0.0;
+        ChunkBuf<DT, PT, VEC> cb;
+        cb.load(p, zrow, qrow, use_resid, jc * kChunk2);
 #pragma unroll
-        for (int i = 0; i < kEpt2; ++i) local += w[i];
-        double ctot;
-        const double excl = block_exclusive_scan(local, sm_d, &ctot);
-        int cand = INT_MAX;
-        if (excl + local > rem) {
-            double cum = excl;
+        for (int g = 0; g < kEpt2 / 8; ++g) {
+            if (tok < 0) {  // uniform
+                const int idx = jc * kChunk2 + (g * kThreads + tid) * 8;
+                double w[8];
+                double local = 0.0;
 #pragma unroll
-            for (int i = 0; i < kEpt2; ++i) {
-                cum += w[i];
-                if (cand == INT_MAX && w[i] > 0.0 && cum > rem) cand = base + i;
+                for (int e = 0; e < 8; ++e) {
+                    w[e] = idx + e < p.V ? draw_weight(p, use_resid, cb.z(g, e), use_resid ? cb.q(g, e) : 0.0f, nMcd, invS)
+                                         : 0.0;
+                    local += w[e];
+                }
+                double gtot;
+                const double excl = block_exclusive_scan(local, sm_d, &gtot);
+                int cand = INT_MAX;
+                if (excl + local > rem) {
+                    double cum = excl;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        cum += w[e];
+                        if (cand == INT_MAX && w[e] > 0.0 && cum > rem) cand = idx + e;
+                    }
+                }
+                cand = block_min_i(cand, sm_i);
+                if (cand != INT_MAX) tok = cand;
+                rem -= gtot;
             }
         }
-        cand = block_min_i(cand, sm_i);
-        if (cand != INT_MAX) tok = cand;
-        rem -= ctot;
         ++jc;
     }
     if (tok < 0) {
-        // u * total at or past the end: largest index with positive weight
+        // u * total at or past the end (only by rounding, u < 1): the largest
+        // index with positive weight, in the last chunk whose weight is > 0
+        int jl = -1;
+        for (int j = tid; j < p.nch2; j += kThreads)
+            if (chunk_weight(j) > 0.0) jl = max(jl, j);
+        jl = block_max_i(jl, sm_i);
         int lastv = -1;
-        for (int j = threadIdx.x; j < p.nch2; j += kThreads) {
-            const uint64_t w = ld_agent(draw_slot(p, b, j) + 3);
-            lastv = max(lastv, use_resid ? (int)(int32_t)(uint32_t)w : (int)(int32_t)(uint32_t)(w >> 32));
+        if (jl >= 0) {
+            ChunkBuf<DT, PT, VEC> cb;
+            cb.load(p, zrow, qrow, use_resid, jl * kChunk2);
+#pragma unroll
+            for (int g = 0; g < kEpt2 / 8; ++g) {
+                const int idx = jl * kChunk2 + (g * kThreads + tid) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (idx + e < p.V &&
+                        draw_weight(p, use_resid, cb.z(g, e), use_resid ? cb.q(g, e) : 0.0f, nMcd, invS) > 0.0)
+                        lastv = max(lastv, idx + e);
+            }
         }
         tok = block_max_i(lastv, sm_i);
     }
     // every read of this sequence's chunk slots ended before a barrier above
     clear_draw_partials(p, b);
-    finish_sequence(p, b, n, tok, false, Z, true);
+    finish_sequence(p, b, n, tok, false, Z, true, pi);
 }
 
 __global__ __launch_bounds__(kThreads) void k_draw_greedy(const DrawParams p)
@@ -965,15 +1103,17 @@ __global__ __launch_bounds__(kThreads) void k_draw_greedy(const DrawParams p)
     // argmax of row n ([FI] "Standardized Sampling", argmax case)
     const int b = blockIdx.x;
     __shared__ int sm_i[kWaves];
+    __shared__ int sm_t;
     const uint64_t m = p.mask[b];
     const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
     const int n = rej ? __builtin_ctzll(rej) : p.gamma;
-    // every thread reads the mask before the barriers in tokens_invalid, and
-    // the mask is cleared only after them (finish_sequence)
-    const bool bad_token = tokens_invalid(p, b, sm_i);
+    const PosInfo pi = load_pos_info(p, b);
+    if ((int)threadIdx.x == n) sm_t = pi.st.amax;
+    // every thread has read the mask before the barriers in tokens_invalid,
+    // and the mask is cleared only after them (finish_sequence)
+    const bool bad_token = tokens_invalid(p, pi, sm_i);
     const bool invalid = (m & kInvalidBit) != 0 || bad_token;
-    const int t = invalid ? -1 : p.stats[(int64_t)b * (p.gamma + 1) + n].amax;
-    finish_sequence(p, b, n, t, invalid, NAN, false);
+    finish_sequence(p, b, n, invalid ? -1 : sm_t, invalid, NAN, false, pi);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail)
@@ -998,18 +1138,24 @@ void launch_rows(bool greedy, bool vec, int grid, const RowParams& rp, hipStream
 }
 
 template <int DT, int PT>
-void launch_draw_sample_t(bool vec, int grid, const DrawParams& dp, hipStream_t s)
+void launch_draw_sample_t(bool vec, int grid_sums, int grid_finish, const DrawParams& dp, hipStream_t s)
 {
-    if (vec) hipLaunchKernelGGL((k_draw_sample<DT, PT, true>), dim3(grid), dim3(kThreads), 0, s, dp);
-    else hipLaunchKernelGGL((k_draw_sample<DT, PT, false>), dim3(grid), dim3(kThreads), 0, s, dp);
+    if (vec) {
+        hipLaunchKernelGGL((k_draw_sums<DT, PT, true>), dim3(grid_sums), dim3(kThreads), 0, s, dp);
+        hipLaunchKernelGGL((k_draw_finish<DT, PT, true>), dim3(grid_finish), dim3(kThreads), 0, s, dp);
+    } else {
+        hipLaunchKernelGGL((k_draw_sums<DT, PT, false>), dim3(grid_sums), dim3(kThreads), 0, s, dp);
+        hipLaunchKernelGGL((k_draw_finish<DT, PT, false>), dim3(grid_finish), dim3(kThreads), 0, s, dp);
+    }
 }
 
-void launch_draw_sample(int dt, int pt, bool vec, int grid, const DrawParams& dp, hipStream_t s)
+void launch_draw_sample(int dt, int pt, bool vec, int grid_sums, int grid_finish, const DrawParams& dp,
+                        hipStream_t s)
 {
-    if (dt == SV_FP32 && pt == SV_FP32) launch_draw_sample_t<SV_FP32, SV_FP32>(vec, grid, dp, s);
-    if (dt == SV_FP32 && pt == SV_BF16) launch_draw_sample_t<SV_FP32, SV_BF16>(vec, grid, dp, s);
-    if (dt == SV_BF16 && pt == SV_FP32) launch_draw_sample_t<SV_BF16, SV_FP32>(vec, grid, dp, s);
-    if (dt == SV_BF16 && pt == SV_BF16) launch_draw_sample_t<SV_BF16, SV_BF16>(vec, grid, dp, s);
+    if (dt == SV_FP32 && pt == SV_FP32) launch_draw_sample_t<SV_FP32, SV_FP32>(vec, grid_sums, grid_finish, dp, s);
+    if (dt == SV_FP32 && pt == SV_BF16) launch_draw_sample_t<SV_FP32, SV_BF16>(vec, grid_sums, grid_finish, dp, s);
+    if (dt == SV_BF16 && pt == SV_FP32) launch_draw_sample_t<SV_BF16, SV_FP32>(vec, grid_sums, grid_finish, dp, s);
+    if (dt == SV_BF16 && pt == SV_BF16) launch_draw_sample_t<SV_BF16, SV_BF16>(vec, grid_sums, grid_finish, dp, s);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -1119,7 +1265,9 @@ int spec_verify(int batch, int gamma, int vocab,
     dp.tokens = draft_tokens;
     dp.uniforms = uniforms;
     dp.mask = rp.mask;
-    dp.cnt2 = reinterpret_cast<uint32_t*>(ws + L.cnt2_off);
+    dp.cnt1 = rp.cnt1;
+    dp.part1 = rp.part1;
+    dp.nch1 = nch1;
     dp.stats = rp.stats;
     dp.part2 = reinterpret_cast<DrawPart*>(ws + L.part2_off);
     dp.n_out = n_accepted;
@@ -1144,7 +1292,7 @@ int spec_verify(int batch, int gamma, int vocab,
     if (extras && extras->ev_mid && hipEventRecord((hipEvent_t)extras->ev_mid, s) != hipSuccess)
         return SV_ERR_LAUNCH;
     if (greedy) hipLaunchKernelGGL(k_draw_greedy, dim3((unsigned)grid2), dim3(kThreads), 0, s, dp);
-    else launch_draw_sample(logits_dtype, probs_dtype, vec2, (int)grid2, dp, s);
+    else launch_draw_sample(logits_dtype, probs_dtype, vec2, (int)grid2, batch, dp, s);
     if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
     if (extras && extras->ev_end && hipEventRecord((hipEvent_t)extras->ev_end, s) != hipSuccess)
         return SV_ERR_LAUNCH;

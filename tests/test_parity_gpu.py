@@ -180,3 +180,24 @@ def test_zz_report_flag_rate():
     print(f"[parity] totals {json.dumps(s)}", flush=True)
     if s["decisions"]:
         assert s["flagged_decisions"] / s["decisions"] < 1e-4
+
+
+def test_uniform_at_interval_ends():
+    # u = 0 draws the first positive-weight token; u = 1 sits on the last
+    # boundary (flagged by the oracle) and must still give a token of the
+    # residual / bonus support at the end of the row
+    import oracle
+    d = synth.make_inputs("c4", 806, B=16, V=20_000)
+    for u_end in (0.0, 1.0):
+        d["uniforms"][:, -1] = u_end
+        g = run_gpu(d)
+        r = run_ref(d)
+        same_walk = g["n_accepted"] == r["n_accepted"]
+        assert np.all(same_walk)
+        n = r["n_accepted"]
+        tok_g = g["out_tokens"][np.arange(d["B"]), n]
+        tok_r = r["out_tokens"][np.arange(d["B"]), n]
+        if u_end == 0.0:
+            assert np.array_equal(tok_g, tok_r)
+        else:
+            assert np.all(np.abs(tok_g - tok_r) < 4096)
