@@ -344,6 +344,61 @@ __device__ __forceinline__ void load_chunk(const void* rowp, int v0, int V, floa
     else load_chunk_impl<DT, VEC, EPT, false>(rowp, v0, V, x);
 }
 
+// This thread's share of one row-stage chunk, kept as loaded: raw 128-bit
+// words on the vector path (bf16 values are unpacked at each use, which
+// costs one integer op and halves the registers), floats otherwise.
+// get8(g, z) yields elements 8g .. 8g+7 in the order of load_chunk.
+template <int DT, bool VEC, int EPT>
+struct ChunkRegs {
+    static constexpr int W = DT == SV_BF16 ? 8 : 4;
+    uint4 raw[EPT / W];
+    __device__ __forceinline__ void load(const void* rowp, int v0, int V)
+    {
+        if (v0 + EPT * kThreads <= V) load_impl<true>(rowp, v0, V);
+        else load_impl<false>(rowp, v0, V);
+    }
+    template <bool FULL>
+    __device__ __forceinline__ void load_impl(const void* rowp, int v0, int V)
+    {
+        constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int j = 0; j < EPT / W; ++j) {
+            int idx = v0 + (j * kThreads + tid) * W;
+            if constexpr (!FULL) idx = min(idx, V - W);
+            raw[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(rowp) + (size_t)idx * ES);
+        }
+        if constexpr (!FULL) {
+            const uint32_t ninf = DT == SV_BF16 ? 0xff80ff80u : 0xff800000u;
+#pragma unroll
+            for (int j = 0; j < EPT / W; ++j)
+                if (v0 + (j * kThreads + tid) * W >= V) raw[j] = make_uint4(ninf, ninf, ninf, ninf);
+        }
+    }
+    __device__ __forceinline__ void get8(int g, float (&z)[8]) const
+    {
+        if constexpr (DT == SV_BF16) {
+            const uint4 w = raw[g];
+            z[0] = bf16_lo(w.x); z[1] = bf16_hi(w.x); z[2] = bf16_lo(w.y); z[3] = bf16_hi(w.y);
+            z[4] = bf16_lo(w.z); z[5] = bf16_hi(w.z); z[6] = bf16_lo(w.w); z[7] = bf16_hi(w.w);
+        } else {
+            const uint4 a = raw[2 * g], b = raw[2 * g + 1];
+            z[0] = __uint_as_float(a.x); z[1] = __uint_as_float(a.y); z[2] = __uint_as_float(a.z); z[3] = __uint_as_float(a.w);
+            z[4] = __uint_as_float(b.x); z[5] = __uint_as_float(b.y); z[6] = __uint_as_float(b.z); z[7] = __uint_as_float(b.w);
+        }
+    }
+};
+template <int DT, int EPT>
+struct ChunkRegs<DT, false, EPT> {
+    float x[EPT];
+    __device__ __forceinline__ void load(const void* rowp, int v0, int V) { load_chunk<DT, false, EPT>(rowp, v0, V, x); }
+    __device__ __forceinline__ void get8(int g, float (&z)[8]) const
+    {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = x[g * 8 + e];
+    }
+};
+
 template <bool VEC, int EPT, int W>
 __device__ __forceinline__ int elem_index(int v0, int e)
 {
@@ -370,6 +425,7 @@ struct RowParams {
 // sequence's reject mask once and broadcasts, so the whole block agrees.
 __device__ __forceinline__ bool chunk_skipped(const RowParams& p, int b, int k, int* sm_flag)
 {
+    if (k == 0) return false;  // position 0 is always needed (k is uniform)
     if (threadIdx.x == 0) {
         const uint64_t m = ld_agent(&p.mask[b]);
         const uint64_t earlier = k == 0 ? 0ull : (m & ((1ull << k) - 1ull));
@@ -417,16 +473,34 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
     __shared__ int sm_flag;
 
     if (chunk_skipped(p, b, k, &sm_flag)) return;
+    // The decision inputs (draft token, its logit and draft probability, the
+    // uniform) are fetched while the chunk streams, in case this block turns
+    // out to be the row's last.
+    int xk = 0;
+    float zx = 0.0f, qx = 0.0f, uk = 0.0f;
+    if (threadIdx.x == 0 && k < p.gamma) {
+        xk = p.tokens[(int64_t)b * p.gamma + k];
+        uk = p.uniforms[(int64_t)b * G1 + k];
+        if (xk >= 0 && xk < p.V) {
+            zx = load_one_rt(p.logits, DT, row * p.V + xk);
+            qx = load_one_rt(p.probs, p.probs_dtype, ((int64_t)b * p.gamma + k) * p.V + xk);
+        }
+    }
     uint32_t dep = 0;
     {
         const int v0 = c * CH;
         const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
-        float x[EPT];
-        load_chunk<DT, VEC, EPT>(rowp, v0, p.V, x);
+        ChunkRegs<DT, VEC, EPT> x;
+        x.load(rowp, v0, p.V);
 
         float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) mx = fmaxf(mx, x[e]);
+        for (int g = 0; g < EPT / 8; ++g) {
+            float z[8];
+            x.get8(g, z);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, z[e]);
+        }
         mx = block_max(mx, sm_f);
 
         double s = 0.0;
@@ -440,12 +514,10 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
             double acc = 0.0;
 #pragma unroll
             for (int g = 0; g < EPT / 8; ++g) {
-                float e8[8];
+                float z[8], e8[8];
+                x.get8(g, z);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float z = x[g * 8 + e];
-                    e8[e] = __builtin_amdgcn_exp2f(fmaf(z, p.c_lo, fmaf(z, p.c_hi, K)));
-                }
+                for (int e = 0; e < 8; ++e) e8[e] = __builtin_amdgcn_exp2f(fmaf(z[e], p.c_lo, fmaf(z[e], p.c_hi, K)));
                 acc += (double)(((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7])));
             }
             s = block_sum(acc, sm_d);
@@ -485,17 +557,14 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         if (k < p.gamma) {
             // [FI] Phase 3 / [PB] section 3: accept x_k iff u_k <= min(1, p/q),
             // q <= 0 accepts ([PB] Reference Implementation).
-            const int x = p.tokens[(int64_t)b * p.gamma + k];
-            if (x < 0 || x >= p.V) {
+            if (xk < 0 || xk >= p.V) {
                 __hip_atomic_fetch_or(&p.mask[b], kInvalidBit | (1ull << k), __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
             } else {
-                const double z = (double)load_one_rt(p.logits, DT, row * p.V + x);
-                const double P = exp2((z - (double)M) * p.cd) / S;
-                const double Q = (double)load_one_rt(p.probs, p.probs_dtype,
-                                                     ((int64_t)b * p.gamma + k) * p.V + x);
+                const double P = exp2(((double)zx - (double)M) * p.cd) / S;
+                const double Q = (double)qx;
                 const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / Q);
-                const double u = (double)p.uniforms[(int64_t)b * G1 + k];
+                const double u = (double)uk;
                 st.P = P;
                 st.Q = Q;
                 if (!(u <= thr))

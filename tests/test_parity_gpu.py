@@ -33,6 +33,29 @@ def _check(d, mode="sample", aux=True):
     return g, r, c
 
 
+# ------------------------------------------------- full sizes (as the benchmark runs them)
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c4_full_size_bench_inputs(seed):
+    # B=256, gamma=8, V=152064 bf16/bf16: the two input sets bench.py times
+    _check(synth.make_inputs("c4", seed))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c3_full_size_sample_and_greedy(seed):
+    d = synth.make_inputs("c3", seed)
+    _check(d)
+    _check(d, mode="greedy", aux=False)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c5_full_size(seed):
+    d = synth.make_inputs("c5", seed)
+    g, r, _ = _check(d)
+    # the always-disjoint row (0, 0) rejects at position 0 in both
+    assert r["n_accepted"][0] == 0 and g["n_accepted"][0] == 0
+
+
 # ---------------------------------------------------------- reduced shapes, many seeds
 
 @pytest.mark.parametrize("seed", range(12))
