@@ -264,6 +264,15 @@ __device__ __forceinline__ void amax_merge(float& v, int& i, float v2, int i2)
 {
     if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
+__device__ __forceinline__ void wave_amax(float& v, int& i)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float v2 = __shfl_xor(v, o, 64);
+        int i2 = __shfl_xor(i, o, 64);
+        amax_merge(v, i, v2, i2);
+    }
+}
 __device__ void block_amax(float& v, int& i, float* smf, int* smi)
 {
 #pragma unroll
@@ -278,6 +287,33 @@ __device__ void block_amax(float& v, int& i, float* smf, int* smi)
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) amax_merge(v, i, smf[w], smi[w]);
     __syncthreads();
+}
+
+// 2^a in double for a <= 0, relative error below 2e-14: a = k + f with k
+// the nearest integer (rounded by adding 1.5 * 2^52, which leaves k in the
+// low word) and |f| <= 1/2; 2^f by a degree-9 polynomial interpolating it at
+// Chebyshev nodes of [-1/2, 1/2]; 2^k is added to the exponent field.  Below
+// -1020 (and for -inf or NaN) the result is 0.
+__device__ __forceinline__ double exp2_f64(double a)
+{
+    const bool tiny = !(a >= -1020.0);
+    a = tiny ? -1020.0 : a;
+    const double magic = 6755399441055744.0;
+    const double t = a + magic;
+    const double f = a - (t - magic);
+    const int k = __double2loint(t);
+    double p = 1.0208789509527192e-07;
+    p = fma(f, p, 1.3259656070717964e-06);
+    p = fma(f, p, 1.5252656913569549e-05);
+    p = fma(f, p, 0.00015403433688494325);
+    p = fma(f, p, 0.0013333558230514875);
+    p = fma(f, p, 0.009618129194063072);
+    p = fma(f, p, 0.05550410866444786);
+    p = fma(f, p, 0.24022650695639422);
+    p = fma(f, p, 0.6931471805599502);
+    p = fma(f, p, 1.0000000000000138);
+    const double r = __hiloint2double(__double2hiint(p) + (int)((unsigned)k << 20), __double2loint(p));
+    return tiny ? 0.0 : r;
 }
 
 // Loads this thread's share of one row-stage chunk into registers.  Vector
@@ -435,23 +471,23 @@ __device__ __forceinline__ bool chunk_skipped(const RowParams& p, int b, int k, 
     return *sm_flag != 0;
 }
 
-// Shared epilogue: count this block in and learn whether it is the last
-// block of the row; the last block resets the counter to zero.  Blocks that
-// skip their chunk never count in, so a row with a skipped chunk has no last
-// block (it is not needed: an earlier position was rejected); the draw stage
-// clears such a row's counter and partial slots.
-__device__ __forceinline__ bool row_arrive(const RowParams& p, int64_t row, uint32_t dep, int* sm_flag)
+// Shared epilogue, run by wave 0 alone once the block's reductions are done
+// (the other waves have left; no block barrier follows): count this block in
+// and learn whether it is the last block of the row; the last block resets
+// the counter to zero.  Blocks that skip their chunk never count in, so a row
+// with a skipped chunk has no last block (it is not needed: an earlier
+// position was rejected); the draw stage clears such a row's counter and
+// partial slots.
+__device__ __forceinline__ bool row_arrive(const RowParams& p, int64_t row, uint32_t dep)
 {
-    __syncthreads();
+    uint32_t last = 0;
     if (threadIdx.x == 0) {
         const uint32_t old = __hip_atomic_fetch_add(&p.cnt1[row], 1u + dep, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old + 1u == (uint32_t)p.nch;
+        last = old + 1u == (uint32_t)p.nch ? 1u : 0u;
         if (last) __hip_atomic_store(&p.cnt1[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *sm_flag = last ? 1 : 0;
     }
-    __syncthreads();
-    return *sm_flag != 0;
+    return __builtin_amdgcn_readfirstlane(last) != 0u;
 }
 
 // ----------------------------------------------------------------- row stage, sample
@@ -522,6 +558,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
             }
             s = block_sum(acc, sm_d);
         }
+        if (threadIdx.x >= 64) return;  // only wave 0 goes on (no block barrier below)
         if (threadIdx.x == 0) {
             if (mx > -INFINITY) s *= exp2(-((double)K + mc));
             const uint64_t w[2] = {(uint64_t)__float_as_uint(mx), (uint64_t)__double_as_longlong(s)};
@@ -529,23 +566,24 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         }
     }
 
-    if (!row_arrive(p, row, dep, &sm_flag)) return;
+    if (!row_arrive(p, row, dep)) return;
 
-    // Last block of a fully processed row: merge the chunk partials.
+    // Last block of a fully processed row: wave 0 merges the chunk partials.
+    const int lane = (int)threadIdx.x;
     float M = -INFINITY;
-    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+    for (int j = lane; j < p.nch; j += 64) {
         const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
         M = fmaxf(M, __uint_as_float((uint32_t)ld_agent(slot)));
     }
-    M = block_max(M, sm_f);
+    M = wave_max(M);
     double S = 0.0;
-    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+    for (int j = lane; j < p.nch; j += 64) {
         const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
         const float mj = __uint_as_float((uint32_t)ld_agent(slot));
         const double sj = __longlong_as_double((long long)ld_agent(slot + 1));
-        if (mj > -INFINITY) S += sj * exp2(((double)mj - (double)M) * p.cd);
+        if (mj > -INFINITY) S += sj * exp2_f64(((double)mj - (double)M) * p.cd);
     }
-    S = block_sum(S, sm_d);
+    S = wave_sum(S);
 
     if (threadIdx.x == 0) {
         RowStat st;
@@ -609,21 +647,22 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
             if (idx < p.V) amax_merge(bv, bi, x[e], idx);
         }
         block_amax(bv, bi, sm_f, sm_i);
+        if (threadIdx.x >= 64) return;  // only wave 0 goes on (no block barrier below)
         if (threadIdx.x == 0) {
             const uint64_t w[1] = {((uint64_t)(uint32_t)bi << 32) | (uint64_t)__float_as_uint(bv)};
             dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
         }
     }
 
-    if (!row_arrive(p, row, dep, &sm_flag)) return;
+    if (!row_arrive(p, row, dep)) return;
 
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int j = threadIdx.x; j < p.nch; j += kThreads) {
+    for (int j = (int)threadIdx.x; j < p.nch; j += 64) {
         const uint64_t w = ld_agent(p.part1 + 2 * ((size_t)row * p.nch + j));
         amax_merge(bv, bi, __uint_as_float((uint32_t)w), (int)(uint32_t)(w >> 32));
     }
-    block_amax(bv, bi, sm_f, sm_i);
+    wave_amax(bv, bi);
     if (threadIdx.x == 0) {
         RowStat st;
         st.m = bv;
@@ -742,33 +781,6 @@ __device__ bool tokens_invalid(const DrawParams& p, const PosInfo& pi, int* sm_i
     const int i = threadIdx.x;
     const int bad = (i < p.gamma && (pi.tok < 0 || pi.tok >= p.V)) ? 1 : 0;
     return block_max_i(bad, sm_i) != 0;
-}
-
-// 2^a in double for a <= 0, relative error below 2e-14: a = k + f with k
-// the nearest integer (rounded by adding 1.5 * 2^52, which leaves k in the
-// low word) and |f| <= 1/2; 2^f by a degree-9 polynomial interpolating it at
-// Chebyshev nodes of [-1/2, 1/2]; 2^k is added to the exponent field.  Below
-// -1020 (and for -inf or NaN) the result is 0.
-__device__ __forceinline__ double exp2_f64(double a)
-{
-    const bool tiny = !(a >= -1020.0);
-    a = tiny ? -1020.0 : a;
-    const double magic = 6755399441055744.0;
-    const double t = a + magic;
-    const double f = a - (t - magic);
-    const int k = __double2loint(t);
-    double p = 1.0208789509527192e-07;
-    p = fma(f, p, 1.3259656070717964e-06);
-    p = fma(f, p, 1.5252656913569549e-05);
-    p = fma(f, p, 0.00015403433688494325);
-    p = fma(f, p, 0.0013333558230514875);
-    p = fma(f, p, 0.009618129194063072);
-    p = fma(f, p, 0.05550410866444786);
-    p = fma(f, p, 0.24022650695639422);
-    p = fma(f, p, 0.6931471805599502);
-    p = fma(f, p, 1.0000000000000138);
-    const double r = __hiloint2double(__double2hiint(p) + (int)((unsigned)k << 20), __double2loint(p));
-    return tiny ? 0.0 : r;
 }
 
 // Loads 8 consecutive elements starting at idx (a multiple of 8 on the
