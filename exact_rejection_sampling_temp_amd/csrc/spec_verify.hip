@@ -292,28 +292,33 @@ __device__ void block_amax(float& v, int& i, float* smf, int* smi)
 // 2^a in double for a <= 0, relative error below 2e-14: a = k + f with k
 // the nearest integer (rounded by adding 1.5 * 2^52, which leaves k in the
 // low word) and |f| <= 1/2; 2^f by a degree-9 polynomial interpolating it at
-// Chebyshev nodes of [-1/2, 1/2]; 2^k is added to the exponent field.  Below
-// -1020 (and for -inf or NaN) the result is 0.
-__device__ __forceinline__ double exp2_f64(double a)
+// Chebyshev nodes of [-1/2, 1/2]; 2^k applied with ldexp, which rounds to a
+// subnormal or to 0 below the normal range.  a is clamped at -1100 first, so
+// -inf (and NaN) give exactly 0.  The coefficients travel as kernel
+// arguments: uniform values stay in scalar registers, which fp64 FMAs read
+// directly (as literals they would be rebuilt in vector registers for every
+// element).
+struct Exp2Coef {
+    double c[10];  // c[0] multiplies f^9, c[9] is the constant term
+    double magic;  // 1.5 * 2^52
+    double lo;     // clamp: -1100
+};
+constexpr Exp2Coef kExp2Coef = {{1.0208789509527192e-07, 1.3259656070717964e-06, 1.5252656913569549e-05,
+                                 0.00015403433688494325, 0.0013333558230514875, 0.009618129194063072,
+                                 0.05550410866444786, 0.24022650695639422, 0.6931471805599502,
+                                 1.0000000000000138},
+                                6755399441055744.0, -1100.0};
+
+__device__ __forceinline__ double exp2_f64(double a, const Exp2Coef& k)
 {
-    const bool tiny = !(a >= -1020.0);
-    a = tiny ? -1020.0 : a;
-    const double magic = 6755399441055744.0;
-    const double t = a + magic;
-    const double f = a - (t - magic);
-    const int k = __double2loint(t);
-    double p = 1.0208789509527192e-07;
-    p = fma(f, p, 1.3259656070717964e-06);
-    p = fma(f, p, 1.5252656913569549e-05);
-    p = fma(f, p, 0.00015403433688494325);
-    p = fma(f, p, 0.0013333558230514875);
-    p = fma(f, p, 0.009618129194063072);
-    p = fma(f, p, 0.05550410866444786);
-    p = fma(f, p, 0.24022650695639422);
-    p = fma(f, p, 0.6931471805599502);
-    p = fma(f, p, 1.0000000000000138);
-    const double r = __hiloint2double(__double2hiint(p) + (int)((unsigned)k << 20), __double2loint(p));
-    return tiny ? 0.0 : r;
+    a = fmax(a, k.lo);
+    const double t = a + k.magic;
+    const double f = a - (t - k.magic);
+    const int n = __double2loint(t);
+    double p = k.c[0];
+#pragma unroll
+    for (int i = 1; i < 10; ++i) p = fma(f, p, k.c[i]);
+    return ldexp(p, n);
 }
 
 // Loads this thread's share of one row-stage chunk into registers.  Vector
@@ -411,6 +416,14 @@ struct ChunkRegs {
                 if (v0 + (j * kThreads + tid) * W >= V) raw[j] = make_uint4(ninf, ninf, ninf, ninf);
         }
     }
+    // Hides the loaded words from the optimizer, so values unpacked before
+    // this point are recomputed after it rather than kept live (the raw
+    // words take half the registers).
+    __device__ __forceinline__ void opaque()
+    {
+#pragma unroll
+        for (int j = 0; j < EPT / W; ++j) asm volatile("" : "+v"(raw[j].x), "+v"(raw[j].y), "+v"(raw[j].z), "+v"(raw[j].w));
+    }
     __device__ __forceinline__ void get8(int g, float (&z)[8]) const
     {
         if constexpr (DT == SV_BF16) {
@@ -428,6 +441,7 @@ template <int DT, int EPT>
 struct ChunkRegs<DT, false, EPT> {
     float x[EPT];
     __device__ __forceinline__ void load(const void* rowp, int v0, int V) { load_chunk<DT, false, EPT>(rowp, v0, V, x); }
+    __device__ __forceinline__ void opaque() {}
     __device__ __forceinline__ void get8(int g, float (&z)[8]) const
     {
 #pragma unroll
@@ -455,6 +469,7 @@ struct RowParams {
     uint32_t zero;     // always 0 (see publish)
     float c_hi, c_lo;  // log2(e)/T split into two fp32 terms, c_lo > 0
     double cd;         // log2(e)/T in double
+    Exp2Coef ex;       // kExp2Coef
 };
 
 // Shared prologue: is this (row, chunk) still needed?  Thread 0 reads the
@@ -538,6 +553,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
             for (int e = 0; e < 8; ++e) mx = fmaxf(mx, z[e]);
         }
         mx = block_max(mx, sm_f);
+        x.opaque();
 
         double s = 0.0;
         double mc = 0.0;
@@ -581,7 +597,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
         const float mj = __uint_as_float((uint32_t)ld_agent(slot));
         const double sj = __longlong_as_double((long long)ld_agent(slot + 1));
-        if (mj > -INFINITY) S += sj * exp2_f64(((double)mj - (double)M) * p.cd);
+        if (mj > -INFINITY) S += sj * exp2_f64(((double)mj - (double)M) * p.cd, p.ex);
     }
     S = wave_sum(S);
 
@@ -706,6 +722,7 @@ struct DrawParams {
     int B, gamma, V, nch2;
     uint32_t zero;  // always 0 (see publish)
     double cd;
+    Exp2Coef ex;  // kExp2Coef
 };
 
 // Per-position values the finish of a sequence needs, loaded early by thread
@@ -866,11 +883,13 @@ __device__ __forceinline__ void draw_chunk_sums(const DrawParams& p, const void*
     // e_v = 2^((z - M) log2(e)/T); the shift -M log2(e)/T is rounded once for
     // the whole row, a common factor that cancels in every ratio used
     auto element = [&](float zf, float qf) {
-        const double e = exp2_f64(fma((double)zf, p.cd, nMcd));
+        const double e = exp2_f64(fma((double)zf, p.cd, nMcd), p.ex);
         E += e;
         if (resid) {
             const double qd = (double)qf;
-            if (e > qd * S_row) { EA += e; QA += qd; }
+            const double in = e > qd * S_row ? 1.0 : 0.0;  // in the residual support
+            EA = fma(e, in, EA);
+            QA = fma(qd, in, QA);
         }
     };
     if constexpr (VEC) {
@@ -907,7 +926,7 @@ __device__ __forceinline__ void draw_chunk_sums(const DrawParams& p, const void*
 __device__ __forceinline__ double draw_weight(const DrawParams& p, bool use_resid, float z, float q, double nMcd,
                                               double invS)
 {
-    const double e = exp2_f64(fma((double)z, p.cd, nMcd));
+    const double e = exp2_f64(fma((double)z, p.cd, nMcd), p.ex);
     return use_resid ? fmax(0.0, e * invS - (double)q) : e;
 }
 
@@ -1339,6 +1358,7 @@ int spec_verify(int batch, int gamma, int vocab,
     rp.c_hi = c_hi;
     rp.c_lo = c_lo;
     rp.cd = cd;
+    rp.ex = kExp2Coef;
 
     DrawParams dp;
     dp.logits = target_logits;
@@ -1364,6 +1384,7 @@ int spec_verify(int batch, int gamma, int vocab,
     dp.nch2 = nch2;
     dp.zero = 0u;
     dp.cd = cd;
+    dp.ex = kExp2Coef;
 
     if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)
         return SV_ERR_LAUNCH;
