@@ -107,7 +107,7 @@ Layout make_layout(int B, int gamma, int V)
     L.nch2_max = (V + kChunk2 - 1) / kChunk2;
     size_t off = 0;
     L.mask_off = off;  off = align256(off + sizeof(uint64_t) * (size_t)B);
-    L.cnt1_off = off;  off = align256(off + sizeof(uint32_t) * rows);
+    L.cnt1_off = off;  off = align256(off + sizeof(uint64_t) * rows);
     L.control_bytes = off;
     L.part1_off = off; off = align256(off + 2 * sizeof(uint64_t) * rows * (size_t)L.nch1_max);
     L.stats_off = off; off = align256(off + sizeof(RowStat) * rows);
@@ -462,7 +462,7 @@ struct RowParams {
     const int32_t* tokens;
     const float* uniforms;
     uint64_t* mask;
-    uint32_t* cnt1;
+    uint64_t* cnt1;   // per row: arrivals (low 16 bits), rejection evidence (high 48)
     uint64_t* part1;  // [rows][nch][2]
     RowStat* stats;
     int B, gamma, V, nch, probs_dtype;
@@ -493,14 +493,42 @@ __device__ __forceinline__ bool chunk_skipped(const RowParams& p, int b, int k, 
 // with a skipped chunk has no last block (it is not needed: an earlier
 // position was rejected); the draw stage clears such a row's counter and
 // partial slots.
-__device__ __forceinline__ bool row_arrive(const RowParams& p, int64_t row, uint32_t dep)
+//
+// The counter word also gathers evidence of a rejection (sample mode): each
+// block adds, in its high 48 bits, floor(2^30 min(2, u Q s')) where s' is its
+// chunk's sum of exp((z_v - z_x)/T) (z_x the draft token's logit).  Every
+// term is positive, so once the running total exceeds 2^30 (plus a margin
+// far above the rounding of these terms) u Q sum_v exp((z_v - z_x)/T) > 1,
+// i.e. p(x) / q(x) < u: the position is rejected whatever the other chunks
+// hold.  The block that sees this sets the reject bit at once, so later
+// positions of the sequence stop being fetched sooner; the last block still
+// takes the full decision, which is the same.
+constexpr int kCountBits = 16;
+constexpr uint64_t kCountMask = (1ull << kCountBits) - 1ull;
+constexpr double kEvidenceScale = 0x1p30;
+constexpr uint64_t kEvidenceThreshold = (1ull << 30) + (1ull << 14);
+
+__device__ __forceinline__ uint64_t rejection_evidence(double u, double Q, double s, float mx, float zx, double cd,
+                                                       const Exp2Coef& ex)
+{
+    if (!(Q > 0.0) || !(mx > -INFINITY)) return 0;
+    const double x = zx > -INFINITY ? u * Q * s * exp2_f64(((double)mx - (double)zx) * cd, ex) : 2.0;
+    return (uint64_t)(fmin(x, 2.0) * kEvidenceScale);
+}
+
+__device__ __forceinline__ bool row_arrive(const RowParams& p, int64_t row, int b, uint64_t evidence,
+                                          uint64_t early_bit, uint32_t dep)
 {
     uint32_t last = 0;
     if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&p.cnt1[row], 1u + dep, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last = old + 1u == (uint32_t)p.nch ? 1u : 0u;
-        if (last) __hip_atomic_store(&p.cnt1[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t add = 1ull + (evidence << kCountBits) + dep;
+        const uint64_t old = __hip_atomic_fetch_add(&p.cnt1[row], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (old & kCountMask) + 1ull == (uint64_t)p.nch ? 1u : 0u;
+        if (last) {
+            __hip_atomic_store(&p.cnt1[row], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (early_bit && (old >> kCountBits) + evidence > kEvidenceThreshold) {
+            __hip_atomic_fetch_or(&p.mask[b], early_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     return __builtin_amdgcn_readfirstlane(last) != 0u;
 }
@@ -538,6 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         }
     }
     uint32_t dep = 0;
+    uint64_t evidence = 0, early_bit = 0;
     {
         const int v0 = c * CH;
         const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
@@ -579,10 +608,14 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
             if (mx > -INFINITY) s *= exp2(-((double)K + mc));
             const uint64_t w[2] = {(uint64_t)__float_as_uint(mx), (uint64_t)__double_as_longlong(s)};
             dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
+            if (k < p.gamma && xk >= 0 && xk < p.V) {
+                evidence = rejection_evidence((double)uk, (double)qx, s, mx, zx, p.cd, p.ex);
+                early_bit = 1ull << k;
+            }
         }
     }
 
-    if (!row_arrive(p, row, dep)) return;
+    if (!row_arrive(p, row, b, evidence, early_bit, dep)) return;
 
     // Last block of a fully processed row: wave 0 merges the chunk partials.
     const int lane = (int)threadIdx.x;
@@ -649,6 +682,13 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
     __shared__ int sm_flag;
 
     if (chunk_skipped(p, b, k, &sm_flag)) return;
+    // the draft token and its logit, for an early rejection by this chunk
+    int xk = -1;
+    float zx = 0.0f;
+    if (threadIdx.x == 0 && k < p.gamma) {
+        xk = p.tokens[(int64_t)b * p.gamma + k];
+        if (xk >= 0 && xk < p.V) zx = load_one_rt(p.logits, DT, row * p.V + xk);
+    }
     uint32_t dep = 0;
     {
         const int v0 = c * CH;
@@ -667,10 +707,14 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
         if (threadIdx.x == 0) {
             const uint64_t w[1] = {((uint64_t)(uint32_t)bi << 32) | (uint64_t)__float_as_uint(bv)};
             dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
+            // an element of this chunk beats the draft token for the argmax
+            // (larger, or equal at a lower index): the position is rejected
+            if (k < p.gamma && xk >= 0 && xk < p.V && bi != INT_MAX && (bv > zx || (bv == zx && bi < xk)))
+                __hip_atomic_fetch_or(&p.mask[b], 1ull << k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
-    if (!row_arrive(p, row, dep)) return;
+    if (!row_arrive(p, row, b, 0, 0, dep)) return;
 
     float bv = -INFINITY;
     int bi = INT_MAX;
@@ -707,7 +751,7 @@ struct DrawParams {
     const int32_t* tokens;
     const float* uniforms;
     uint64_t* mask;
-    uint32_t* cnt1;   // row-stage counters and partial slots, cleared per sequence
+    uint64_t* cnt1;   // row-stage counters and partial slots, cleared per sequence
     uint64_t* part1;
     int nch1;
     RowStat* stats;
@@ -778,7 +822,7 @@ __device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool i
         st_agent(slot + 1, 0ull);
     }
     for (int i = threadIdx.x; i < G1; i += kThreads)
-        __hip_atomic_store(&p.cnt1[(int64_t)b * G1 + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.cnt1[(int64_t)b * G1 + i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x == 0) {
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = (!invalid && sample && n < p.gamma) ? Z : NAN;
@@ -1346,7 +1390,7 @@ int spec_verify(int batch, int gamma, int vocab,
     rp.tokens = draft_tokens;
     rp.uniforms = uniforms;
     rp.mask = reinterpret_cast<uint64_t*>(ws + L.mask_off);
-    rp.cnt1 = reinterpret_cast<uint32_t*>(ws + L.cnt1_off);
+    rp.cnt1 = reinterpret_cast<uint64_t*>(ws + L.cnt1_off);
     rp.part1 = reinterpret_cast<uint64_t*>(ws + L.part1_off);
     rp.stats = reinterpret_cast<RowStat*>(ws + L.stats_off);
     rp.B = batch;
