@@ -11,40 +11,49 @@
 //   [ST] "The exact decoding shortcut that burns compute when guesses miss":
 //        correction_distribution (target row when the residual mass <= 1e-15).
 //
-// Three launches per call (two in greedy mode), all on the caller's stream:
+// Sample mode is three launches on the caller's stream:
 //
-//   1. row stage (k_rows_sample / k_rows_greedy).  The grid enumerates
-//      (position k, sequence b, chunk c) with k slowest.  A workgroup streams
-//      one chunk of target row (b, k) with 128-bit loads and reduces it to a
-//      partial (max, sum of exp) -- or (max, first argmax) in greedy mode --
-//      and the last workgroup of a row (arrival counter) merges the row's
-//      partials and takes the acceptance decision for position k, setting
-//      bit k of the sequence's reject mask on a rejection.  A workgroup that
-//      finds an earlier position of its sequence already rejected skips its
-//      chunk: rows past the first rejection are never needed ([FI] Phase 3,
-//      the walk stops at the first rejection), so with position-major launch
-//      order most of them are never read.  The decision at each position is
-//      independent of the others, so skipping changes no result.
+//   1. k_main_sample.  The grid enumerates (position k, sequence b, chunk c)
+//      with k slowest.  A workgroup streams one chunk of target row (b, k)
+//      with 128-bit loads and reduces it to a partial (max, sum of exp); the
+//      last workgroup of a row (arrival counter) merges the row's partials,
+//      takes the acceptance decision for position k and publishes the row's
+//      statistics.  Rows past the first rejection are never needed ([FI]
+//      Phase 3: the walk stops at the first rejection), so a workgroup that
+//      finds an earlier position of its sequence rejected skips its chunk;
+//      with position-major launch order most unneeded rows are never read.
+//      From a middle position on, once every position up to the first
+//      rejection n is decided, such a workgroup works on the draw of its
+//      sequence instead: it claims one draw chunk of row n (the residual
+//      max(0, p_n - q_n), or p_gamma when n = gamma) and computes its fp64
+//      sums, so the draw of most sequences overlaps the row work of others.
 //
-//   2. draw stage (k_draw_sums + k_draw_finish, or k_draw_greedy).  n is the
-//      index of the lowest set bit of the reject mask (gamma if none).  For
-//      every sequence the row n of the target (and of the draft, when
-//      n < gamma) is streamed in chunks; each workgroup computes, in double
-//      precision, e_v = exp((z_v - max)/T) and the chunk sums needed for the
-//      residual mass.  Then one workgroup per sequence turns them into the
-//      exact row normaliser, picks the chunk holding the inverse-CDF target
-//      and scans it to find the token.
+//   2. k_rest_sample.  Workgroups claim the draw chunks the first launch
+//      left, the sequences resolved last first.
+//
+//   3. k_finish_sample.  One wave per sequence turns the chunk sums into the
+//      inverse-CDF draw, writes the outputs and clears the sequence's
+//      workspace.
+//
+// Greedy mode is k_rows_greedy (same grid; chunk argmax) and k_draw_greedy.
 //
 // Numerics.  The row stage uses fp32 exp2 with a two-term log2(e)/T and a
 // per-chunk correction of the rounded shift, and accumulates in fp64; the
-// acceptance threshold is formed in fp64.  The draw stage works entirely in
-// fp64 (e_v, normaliser, residual, prefix sums), so its token boundaries
-// agree with an fp64 evaluation to rounding level.
+// acceptance threshold is formed in fp64.  The draw works entirely in fp64
+// (e_v, normaliser, residual, prefix sums), so its token boundaries agree
+// with an fp64 evaluation to rounding level.
 //
-// Workspace: reject masks and arrival counters, then scratch for partials
-// and per-row statistics.  It must be all zero before a call, and each
-// consumer clears what it read, so a finished call leaves all of it zero
-// again -- whatever shape the next call has.
+// Cross-workgroup data (row partials, row statistics, draw sums) are
+// written with device-scope atomic exchanges whose returned values feed the
+// operand of the atomic that announces them (an arrival counter or a
+// decision bit), so they are complete device-wide before anyone can learn
+// of them; readers use device-scope atomic loads.
+//
+// Workspace: per-sequence control words and per-row arrival counters, then
+// scratch for partials, row statistics and draw sums.  It must be all zero
+// before a call; the last user of each sequence's part clears it, so a
+// finished call leaves all of it zero again, whatever shape the next call
+// has.
 
 #include <hip/hip_runtime.h>
 
@@ -68,11 +77,24 @@ constexpr int kEptBf16 = 64;
 constexpr int kEptFp32 = 32;
 constexpr int kChunkBf16 = kEptBf16 * kThreads;  // 16384 elements
 constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
-// Elements per thread of one draw-stage chunk (a chunk is 8192 elements).
-constexpr int kEpt2 = 32;
-constexpr int kChunk2 = kEpt2 * kThreads;
 
-// Per-row statistics written by the row stage, read by the draw stage.
+// Draw geometry.  A sub-chunk is 512 consecutive elements of row n, 8 per
+// lane of one wave; a wave takes 4 consecutive sub-chunks and a draw chunk
+// (one claim) is the 4 waves of a workgroup: 8192 elements.
+constexpr int kSub = 512;
+constexpr int kSubPerWave = 4;
+constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16
+constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
+constexpr int kRound = 64 * 8;                      // sub-sums per finish round
+// Workgroups of the row stage that find their row unneeded take draw chunks
+// from this position on (earlier positions stream while most of the rows
+// are still needed, and HBM is the shared bottleneck then).
+#ifndef SV_HELP_FROM
+#define SV_HELP_FROM 3
+#endif
+constexpr int kHelpFrom = SV_HELP_FROM;
+
+// Per-row statistics written by the row stage.
 struct RowStat {
     float m;       // row max of the raw logits
     int32_t amax;  // greedy: first index attaining m
@@ -82,19 +104,29 @@ struct RowStat {
 };
 static_assert(sizeof(RowStat) == 32, "RowStat layout");
 
-// Per-chunk partial of the draw stage.
-struct DrawPart {
-    double E;   // sum of e_v over the chunk
-    double EA;  // sum of e_v over {v : p_v > q_v} (residual support)
-    double QA;  // sum of q_v over the same set
+// Draw sums of one sub-chunk of row n.
+struct SubSum {
+    double E;   // sum of e_v = exp((z_v - m)/T)
+    double EA;  // sum of e_v over A = {v : e_v > q_v S_row} (residual support)
+    double QA;  // sum of q_v over A
     double pad;
 };
-static_assert(sizeof(DrawPart) == 32, "DrawPart layout");
+static_assert(sizeof(SubSum) == 32, "SubSum layout");
+
+// Per-sequence control words.
+struct SeqCtl {
+    uint64_t mask;    // bit k: position k rejected; kInvalidBit: a bad draft token
+    uint64_t dec;     // bit k: position k decided (a rejection also sets every
+                      // later bit); bit gamma: row gamma's statistics out
+    uint64_t claim;   // draw chunks claimed so far
+    uint64_t pad;
+};
+static_assert(sizeof(SeqCtl) == 32, "SeqCtl layout");
 
 struct Layout {
-    size_t mask_off, cnt1_off, control_bytes;
-    size_t part1_off, stats_off, part2_off, total;
-    int nch1_max, nch2_max;
+    size_t ctl_off, cnt1_off, ready_off, rank_off, rcnt_off, control_bytes;
+    size_t part1_off, stats_off, sub_off, total;
+    int nch1_max, nch2, nsub;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -104,14 +136,18 @@ Layout make_layout(int B, int gamma, int V)
     Layout L;
     const size_t rows = (size_t)B * (size_t)(gamma + 1);
     L.nch1_max = (V + kChunkFp32 - 1) / kChunkFp32;
-    L.nch2_max = (V + kChunk2 - 1) / kChunk2;
+    L.nch2 = (V + kChunk2 - 1) / kChunk2;
+    L.nsub = L.nch2 * kSubPerChunk;
     size_t off = 0;
-    L.mask_off = off;  off = align256(off + sizeof(uint64_t) * (size_t)B);
+    L.ctl_off = off;   off = align256(off + sizeof(SeqCtl) * (size_t)B);
     L.cnt1_off = off;  off = align256(off + sizeof(uint64_t) * rows);
+    L.ready_off = off; off = align256(off + sizeof(int32_t) * (size_t)B);
+    L.rank_off = off;  off = align256(off + sizeof(int32_t) * (size_t)B);
+    L.rcnt_off = off;  off = align256(off + sizeof(uint32_t));
     L.control_bytes = off;
     L.part1_off = off; off = align256(off + 2 * sizeof(uint64_t) * rows * (size_t)L.nch1_max);
     L.stats_off = off; off = align256(off + sizeof(RowStat) * rows);
-    L.part2_off = off; off = align256(off + sizeof(DrawPart) * (size_t)B * (size_t)L.nch2_max);
+    L.sub_off = off;   off = align256(off + sizeof(SubSum) * (size_t)B * (size_t)L.nsub);
     L.total = off;
     return L;
 }
@@ -122,28 +158,61 @@ __device__ __forceinline__ uint64_t ld_agent(const uint64_t* p)
 {
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v)
+__device__ __forceinline__ double ld_agent_d(const double* p)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __longlong_as_double((long long)ld_agent(reinterpret_cast<const uint64_t*>(p)));
 }
+__device__ __forceinline__ uint64_t xchg_agent(uint64_t* p, uint64_t v)
+{
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t or_agent(uint64_t* p, uint64_t v)
+{
+    return __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t add_agent64(uint64_t* p, uint64_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fold64(uint64_t v) { return (uint32_t)(v ^ (v >> 32)); }
+__device__ __forceinline__ uint64_t dbits(double d) { return (uint64_t)__double_as_longlong(d); }
 
-// Publishes a block's partial result for the last block of its row or
-// sequence.  Each word goes out with a device-scope atomic exchange, and the
-// exchanged-out old values feed the operand of the caller's arrival-counter
-// increment, so every exchange has completed device-wide before the count
-// that reveals it can be observed.  The last block reads the words back with
-// device-scope atomic loads.  (A release/acquire pair at agent scope orders
-// the same thing but writes back the whole L2 on every block, about ten times
-// the cost of the streaming work itself.)  `zero` is a kernel argument that
-// is always 0 and opaque to the compiler; the result is always 0.
+// Publishes words for the last reader: each goes out with a device-scope
+// atomic exchange, and the caller makes the exchanged-out old values an
+// operand of the atomic that announces the data, so every exchange has
+// completed device-wide before that announcement can be observed.  (A
+// release/acquire pair at agent scope orders the same thing but writes back
+// the whole L2 on every workgroup, about ten times the cost of the streaming
+// work itself.)  `zero` is a kernel argument that is always 0 and opaque to
+// the compiler; the result is always 0.
 template <int N>
 __device__ __forceinline__ uint32_t publish(uint64_t* slot, const uint64_t (&w)[N], uint32_t zero)
 {
     uint64_t dep = 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-        dep ^= __hip_atomic_exchange(slot + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return (uint32_t)(dep ^ (dep >> 32)) & zero;
+    for (int i = 0; i < N; ++i) dep ^= xchg_agent(slot + i, w[i]);
+    return fold64(dep) & zero;
+}
+
+__device__ __forceinline__ uint64_t stat_word0(float m, int32_t amax)
+{
+    return (uint64_t)__float_as_uint(m) | ((uint64_t)(uint32_t)amax << 32);
+}
+__device__ __forceinline__ RowStat ld_stat(const RowStat* s)
+{
+    const uint64_t* w = reinterpret_cast<const uint64_t*>(s);
+    const uint64_t w0 = ld_agent(w), w1 = ld_agent(w + 1), w2 = ld_agent(w + 2), w3 = ld_agent(w + 3);
+    RowStat r;
+    r.m = __uint_as_float((uint32_t)w0);
+    r.amax = (int32_t)(uint32_t)(w0 >> 32);
+    r.S = __longlong_as_double((long long)w1);
+    r.P = __longlong_as_double((long long)w2);
+    r.Q = __longlong_as_double((long long)w3);
+    return r;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -182,12 +251,24 @@ __device__ __forceinline__ int wave_max_i(int v)
     for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
     return v;
 }
-__device__ __forceinline__ int wave_min_i(int v)
+__device__ __forceinline__ uint32_t wave_xor(uint32_t v)
 {
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    for (int o = 32; o > 0; o >>= 1) v ^= (uint32_t)__shfl_xor((int)v, o, 64);
     return v;
 }
+// Inclusive prefix sum over the 64 lanes of a wave (lane order).
+__device__ __forceinline__ double wave_incl_scan(double v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+__device__ __forceinline__ int first_lane(uint64_t ballot) { return ballot ? __builtin_ctzll(ballot) : -1; }
 
 // Block reductions over kThreads threads; every thread gets the result.
 // `sm` must hold kWaves entries and is free again on return.
@@ -202,17 +283,6 @@ __device__ float block_max(float v, float* sm)
     __syncthreads();
     return r;
 }
-__device__ double block_sum(double v, double* sm)
-{
-    v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double r = sm[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) r += sm[w];
-    __syncthreads();
-    return r;
-}
 __device__ int block_max_i(int v, int* sm)
 {
     v = wave_max_i(v);
@@ -224,39 +294,16 @@ __device__ int block_max_i(int v, int* sm)
     __syncthreads();
     return r;
 }
-__device__ int block_min_i(int v, int* sm)
+__device__ double block_sum(double v, double* sm)
 {
-    v = wave_min_i(v);
+    v = wave_sum(v);
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
     __syncthreads();
-    int r = sm[0];
+    double r = sm[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = min(r, sm[w]);
+    for (int w = 1; w < kWaves; ++w) r += sm[w];
     __syncthreads();
     return r;
-}
-
-// Exclusive prefix sum over the block (thread order); also returns the total.
-__device__ double block_exclusive_scan(double v, double* sm, double* total)
-{
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        double t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) sm[wid] = incl;
-    __syncthreads();
-    double base = 0.0, tot = 0.0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        if (w < wid) base += sm[w];
-        tot += sm[w];
-    }
-    __syncthreads();
-    *total = tot;
-    return base + incl - v;
 }
 
 // Argmax pairs: larger value wins, ties go to the lower index.
@@ -275,12 +322,7 @@ __device__ __forceinline__ void wave_amax(float& v, int& i)
 }
 __device__ void block_amax(float& v, int& i, float* smf, int* smi)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        float v2 = __shfl_xor(v, o, 64);
-        int i2 = __shfl_xor(i, o, 64);
-        amax_merge(v, i, v2, i2);
-    }
+    wave_amax(v, i);
     if ((threadIdx.x & 63) == 0) { smf[threadIdx.x >> 6] = v; smi[threadIdx.x >> 6] = i; }
     __syncthreads();
     v = smf[0]; i = smi[0];
@@ -289,35 +331,33 @@ __device__ void block_amax(float& v, int& i, float* smf, int* smi)
     __syncthreads();
 }
 
-// 2^a in double for a <= 0, relative error below 2e-14: a = k + f with k
+// 2^a in double for a <= 0, relative error below 1.1e-12: a = k + f with k
 // the nearest integer (rounded by adding 1.5 * 2^52, which leaves k in the
-// low word) and |f| <= 1/2; 2^f by a degree-9 polynomial interpolating it at
-// Chebyshev nodes of [-1/2, 1/2]; 2^k applied with ldexp, which rounds to a
-// subnormal or to 0 below the normal range.  a is clamped at -1100 first, so
-// -inf (and NaN) give exactly 0.  The coefficients travel as kernel
+// low word) and |f| <= 1/2; 2^f by the degree-8 polynomial interpolating it
+// at the Chebyshev nodes of [-1/2, 1/2]; 2^k applied with ldexp, which
+// rounds to a subnormal or to 0 below the normal range.  a is clamped at
+// -1100 first, so -inf gives exactly 0.  The coefficients travel as kernel
 // arguments: uniform values stay in scalar registers, which fp64 FMAs read
 // directly (as literals they would be rebuilt in vector registers for every
-// element).
+// element); the clamp and the rounding constant have 32-bit literal forms.
 struct Exp2Coef {
-    double c[10];  // c[0] multiplies f^9, c[9] is the constant term
-    double magic;  // 1.5 * 2^52
-    double lo;     // clamp: -1100
+    double c[8];  // c[0] multiplies f^8, c[7] multiplies f; the constant term is 1
 };
-constexpr Exp2Coef kExp2Coef = {{1.0208789509527192e-07, 1.3259656070717964e-06, 1.5252656913569549e-05,
-                                 0.00015403433688494325, 0.0013333558230514875, 0.009618129194063072,
-                                 0.05550410866444786, 0.24022650695639422, 0.6931471805599502,
-                                 1.0000000000000138},
-                                6755399441055744.0, -1100.0};
+constexpr Exp2Coef kExp2Coef = {{1.3255224896485456e-06, 1.531007940249117e-05, 0.00015403455852368108,
+                                 0.0013333450567999416, 0.009618129159402676, 0.05550410941205935,
+                                 0.2402265069581299, 0.6931471805459335}};
 
 __device__ __forceinline__ double exp2_f64(double a, const Exp2Coef& k)
 {
-    a = fmax(a, k.lo);
-    const double t = a + k.magic;
-    const double f = a - (t - k.magic);
+    constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
+    a = __builtin_fmax(a, -1100.0);
+    const double t = a + kMagic;
+    const double f = a - (t - kMagic);
     const int n = __double2loint(t);
     double p = k.c[0];
 #pragma unroll
-    for (int i = 1; i < 10; ++i) p = fma(f, p, k.c[i]);
+    for (int i = 1; i < 8; ++i) p = fma(f, p, k.c[i]);
+    p = fma(f, p, 1.0);
     return ldexp(p, n);
 }
 
@@ -416,6 +456,22 @@ struct ChunkRegs {
                 if (v0 + (j * kThreads + tid) * W >= V) raw[j] = make_uint4(ninf, ninf, ninf, ninf);
         }
     }
+    // Signed 16-bit maximum of the raw bf16 patterns (bf16 vector path): it
+    // is the float maximum whenever it is >= 0 (a positive pattern exceeds
+    // every negative one, and positive patterns order like their values).
+    __device__ __forceinline__ int max_bits16() const
+    {
+        typedef short s2 __attribute__((ext_vector_type(2)));
+        s2 acc = __builtin_bit_cast(s2, raw[0].x);
+#pragma unroll
+        for (int j = 0; j < EPT / W; ++j) {
+            if (j > 0) acc = __builtin_elementwise_max(acc, __builtin_bit_cast(s2, raw[j].x));
+            acc = __builtin_elementwise_max(acc, __builtin_bit_cast(s2, raw[j].y));
+            acc = __builtin_elementwise_max(acc, __builtin_bit_cast(s2, raw[j].z));
+            acc = __builtin_elementwise_max(acc, __builtin_bit_cast(s2, raw[j].w));
+        }
+        return max((int)acc.x, (int)acc.y);
+    }
     // Hides the loaded words from the optimizer, so values unpacked before
     // this point are recomputed after it rather than kept live (the raw
     // words take half the registers).
@@ -456,53 +512,107 @@ __device__ __forceinline__ int elem_index(int v0, int e)
     else return v0 + e * kThreads + (int)threadIdx.x;
 }
 
-struct RowParams {
+// 8 consecutive elements as raw 128-bit words (one for bf16, two for fp32).
+struct Raw8 {
+    uint4 a, b;
+};
+template <int DT>
+__device__ __forceinline__ float raw8_elem(const Raw8& r, int e)
+{
+    if constexpr (DT == SV_BF16) {
+        const uint32_t w = e < 2 ? r.a.x : e < 4 ? r.a.y : e < 6 ? r.a.z : r.a.w;
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+        const uint32_t w = e == 0 ? r.a.x : e == 1 ? r.a.y : e == 2 ? r.a.z : e == 3 ? r.a.w
+                         : e == 4 ? r.b.x : e == 5 ? r.b.y : e == 6 ? r.b.z : r.b.w;
+        return __uint_as_float(w);
+    }
+}
+
+// The 8 elements idx .. idx+7 of a row.  Vector path (idx a multiple of 8,
+// 16-byte aligned row): 128-bit loads, the address clamped to the row when
+// the group ends past V (the caller ignores elements >= V).  Scalar path:
+// element loads, indices clamped to the row.
+template <int DT, bool VEC2>
+__device__ __forceinline__ Raw8 load_group(const void* rowp, int idx, int V)
+{
+    constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
+    Raw8 r;
+    if constexpr (VEC2) {
+        const int ci = min(idx, V - 8);
+        const char* ptr = static_cast<const char*>(rowp) + (size_t)ci * ES;
+        r.a = *reinterpret_cast<const uint4*>(ptr);
+        if constexpr (DT == SV_FP32) r.b = *reinterpret_cast<const uint4*>(ptr + 16);
+        else r.b = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = min(idx + e, V - 1);
+            if constexpr (DT == SV_BF16) w[e] = static_cast<const uint16_t*>(rowp)[i];
+            else w[e] = static_cast<const uint32_t*>(rowp)[i];
+        }
+        if constexpr (DT == SV_BF16) {
+            r.a = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
+            r.b = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            r.a = make_uint4(w[0], w[1], w[2], w[3]);
+            r.b = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    }
+    return r;
+}
+
+// ------------------------------------------------------------------ parameters
+
+struct Params {
     const void* logits;
     const void* probs;
     const int32_t* tokens;
     const float* uniforms;
-    uint64_t* mask;
+    SeqCtl* ctl;
     uint64_t* cnt1;   // per row: arrivals (low 16 bits), rejection evidence (high 48)
-    uint64_t* part1;  // [rows][nch][2]
-    RowStat* stats;
-    int B, gamma, V, nch, probs_dtype;
+    uint64_t* part1;  // [rows][nch1][2]
+    RowStat* stats;   // [rows]
+    SubSum* sub;      // [B][nsub]
+    int32_t* ready;   // [B] sequences in the order their n became known
+    int32_t* rank;    // [B] position of each sequence in `ready`
+    uint32_t* ready_cnt;
+    int32_t* n_out;
+    int32_t* tok_out;
+    double* aux_p;
+    double* aux_q;
+    double* aux_resid;
+    float* aux_rmax;
+    double* aux_rsum;
+    int B, gamma, V, nch1, nch2, nsub, probs_dtype;
     uint32_t zero;     // always 0 (see publish)
     float c_hi, c_lo;  // log2(e)/T split into two fp32 terms, c_lo > 0
     double cd;         // log2(e)/T in double
     Exp2Coef ex;       // kExp2Coef
 };
 
-// Shared prologue: is this (row, chunk) still needed?  Thread 0 reads the
-// sequence's reject mask once and broadcasts, so the whole block agrees.
-__device__ __forceinline__ bool chunk_skipped(const RowParams& p, int b, int k, int* sm_flag)
+// bits 0 .. gamma (one per row of a sequence)
+__device__ __forceinline__ uint64_t rows_mask(int gamma) { return (2ull << gamma) - 1ull; }
+// n from a reject mask: the first rejected position, gamma if none
+__device__ __forceinline__ int first_reject(uint64_t mask, int gamma)
 {
-    if (k == 0) return false;  // position 0 is always needed (k is uniform)
-    if (threadIdx.x == 0) {
-        const uint64_t m = ld_agent(&p.mask[b]);
-        const uint64_t earlier = k == 0 ? 0ull : (m & ((1ull << k) - 1ull));
-        *sm_flag = ((m & kInvalidBit) | earlier) ? 1 : 0;
-    }
-    __syncthreads();
-    return *sm_flag != 0;
+    const uint64_t rej = mask & ((1ull << gamma) - 1ull);
+    return rej ? __builtin_ctzll(rej) : gamma;
 }
 
-// Shared epilogue, run by wave 0 alone once the block's reductions are done
-// (the other waves have left; no block barrier follows): count this block in
-// and learn whether it is the last block of the row; the last block resets
-// the counter to zero.  Blocks that skip their chunk never count in, so a row
-// with a skipped chunk has no last block (it is not needed: an earlier
-// position was rejected); the draw stage clears such a row's counter and
-// partial slots.
-//
-// The counter word also gathers evidence of a rejection (sample mode): each
-// block adds, in its high 48 bits, floor(2^30 min(2, u Q s')) where s' is its
-// chunk's sum of exp((z_v - z_x)/T) (z_x the draft token's logit).  Every
-// term is positive, so once the running total exceeds 2^30 (plus a margin
-// far above the rounding of these terms) u Q sum_v exp((z_v - z_x)/T) > 1,
-// i.e. p(x) / q(x) < u: the position is rejected whatever the other chunks
-// hold.  The block that sees this sets the reject bit at once, so later
-// positions of the sequence stop being fetched sooner; the last block still
-// takes the full decision, which is the same.
+// ------------------------------------------------------------- row stage helpers
+
+// The counter word of a row also gathers evidence of a rejection (sample
+// mode): each block adds, in its high 48 bits, floor(2^30 min(2, u Q s'))
+// where s' is its chunk's sum of exp((z_v - z_x)/T) (z_x the draft token's
+// logit).  Every term is positive, so once the running total exceeds 2^30
+// (plus a margin far above the rounding of these terms)
+// u Q sum_v exp((z_v - z_x)/T) > 1, i.e. p(x) / q(x) < u: the position is
+// rejected whatever the other chunks hold.  The block that sees this sets
+// the reject bit at once, so later positions of the sequence stop being
+// fetched sooner; the last block still takes the full decision, which is
+// the same.
 constexpr int kCountBits = 16;
 constexpr uint64_t kCountMask = (1ull << kCountBits) - 1ull;
 constexpr double kEvidenceScale = 0x1p30;
@@ -516,42 +626,414 @@ __device__ __forceinline__ uint64_t rejection_evidence(double u, double Q, doubl
     return (uint64_t)(fmin(x, 2.0) * kEvidenceScale);
 }
 
-__device__ __forceinline__ bool row_arrive(const RowParams& p, int64_t row, int b, uint64_t evidence,
+// Run by thread 0's wave once the block's reductions are done: count this
+// block in and learn whether it is the last block of the row; the last
+// block resets the counter to zero.  Blocks that skip their chunk never
+// count in, so a row with a skipped chunk has no last block (it is not
+// needed: an earlier position was rejected); the sequence's last user
+// clears such a row's counter.
+__device__ __forceinline__ bool row_arrive(const Params& p, int64_t row, int b, uint64_t evidence,
                                           uint64_t early_bit, uint32_t dep)
 {
     uint32_t last = 0;
     if (threadIdx.x == 0) {
         const uint64_t add = 1ull + (evidence << kCountBits) + dep;
         const uint64_t old = __hip_atomic_fetch_add(&p.cnt1[row], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = (old & kCountMask) + 1ull == (uint64_t)p.nch ? 1u : 0u;
+        last = (old & kCountMask) + 1ull == (uint64_t)p.nch1 ? 1u : 0u;
         if (last) {
             __hip_atomic_store(&p.cnt1[row], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else if (early_bit && (old >> kCountBits) + evidence > kEvidenceThreshold) {
-            __hip_atomic_fetch_or(&p.mask[b], early_bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            or_agent(&p.ctl[b].mask, early_bit);
         }
     }
     return __builtin_amdgcn_readfirstlane(last) != 0u;
 }
 
-// ----------------------------------------------------------------- row stage, sample
+// ------------------------------------------------------------------ draw
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
+// Sums of one wave's 4 sub-chunks s0 .. s0+3 of row n of sequence b, in
+// fp64: E = sum e_v with e_v = 2^((z_v - m) log2(e)/T) (m the row max; the
+// shift -m log2(e)/T is rounded once for the row, a common factor that
+// cancels in every ratio used), and for a residual draw EA, QA over
+// A = {v : e_v > q_v S_row}.  S_row, the row stage's normaliser, only
+// decides membership of A; the exact normaliser is the sum of E.  The sums
+// are published to the sub-chunk slots and the wave counts itself in;
+// returns true (wave-uniform) for the last wave task of the sequence.
+template <int DT, int PT, bool VEC2, bool RESID, bool FULL>
+__device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow, const void* qrow, int s0,
+                                               double nMcd, double S_row, double& mE, double& mEA, double& mQA)
 {
+    const int lane = threadIdx.x & 63;
+    Raw8 zr[kSubPerWave], qr[kSubPerWave];
+#pragma unroll
+    for (int g = 0; g < kSubPerWave; ++g) zr[g] = load_group<DT, VEC2>(zrow, (s0 + g) * kSub + lane * 8, p.V);
+    if constexpr (RESID) {
+#pragma unroll
+        for (int g = 0; g < kSubPerWave; ++g) qr[g] = load_group<PT, VEC2>(qrow, (s0 + g) * kSub + lane * 8, p.V);
+    }
+#pragma unroll
+    for (int g = 0; g < kSubPerWave; ++g) {
+        const int idx = (s0 + g) * kSub + lane * 8;
+        double E = 0.0, EA = 0.0, QA = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const bool ok = FULL || idx + e < p.V;
+            double ev = exp2_f64(fma((double)raw8_elem<DT>(zr[g], e), p.cd, nMcd), p.ex);
+            if constexpr (!FULL) ev = ok ? ev : 0.0;
+            E += ev;
+            if constexpr (RESID) {
+                const double qd = (double)raw8_elem<PT>(qr[g], e);
+                // 1.0 if v is in the residual support, else 0.0
+                const double in = __hiloint2double((ok && ev > qd * S_row) ? 0x3ff00000 : 0, 0);
+                EA = fma(ev, in, EA);
+                QA = fma(qd, in, QA);
+            }
+        }
+        E = wave_sum(E);
+        if constexpr (RESID) {
+            EA = wave_sum(EA);
+            QA = wave_sum(QA);
+        }
+        if (lane == g) { mE = E; mEA = EA; mQA = QA; }
+    }
+}
+
+template <int DT, int PT, bool VEC2>
+__device__ void draw_wave(const Params& p, int b, int s0, uint64_t mask)
+{
+    const int lane = threadIdx.x & 63;
+    const int n = first_reject(mask, p.gamma);
+    const bool resid = n < p.gamma;
+    double mE = 0.0, mEA = 0.0, mQA = 0.0;  // lane g < 4 keeps sub-chunk s0 + g
+    if (!(mask & kInvalidBit)) {
+        const int64_t row = (int64_t)b * (p.gamma + 1) + n;
+        const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
+        const uint64_t w0 = ld_agent(sw), w1 = ld_agent(sw + 1);
+        const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+        const void* qrow = static_cast<const char*>(p.probs) +
+                           (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
+        const double nMcd = -(double)__uint_as_float((uint32_t)w0) * p.cd;
+        const double S_row = __longlong_as_double((long long)w1);
+        const bool full = (s0 + kSubPerWave) * kSub <= p.V;
+        if (resid) {
+            if (full) draw_wave_sums<DT, PT, VEC2, true, true>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
+            else draw_wave_sums<DT, PT, VEC2, true, false>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
+        } else {
+            if (full) draw_wave_sums<DT, PT, VEC2, false, true>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
+            else draw_wave_sums<DT, PT, VEC2, false, false>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
+        }
+    }
+    // lane g < 4 writes sub-chunk s0 + g (read by the finishing launch)
+    if (lane < kSubPerWave) p.sub[(size_t)b * p.nsub + s0 + lane] = SubSum{mE, mEA, mQA, 0.0};
+}
+
+// Weight of one element of row n for the inverse-CDF draw: max(0, p - q)
+// with p = e / S, or e itself for the bonus / fallback draw.
+__device__ __forceinline__ double draw_weight(const Params& p, bool use_resid, float z, float q, double nMcd,
+                                              double invS)
+{
+    const double e = exp2_f64(fma((double)z, p.cd, nMcd), p.ex);
+    return use_resid ? fmax(0.0, e * invS - (double)q) : e;
+}
+
+// Clears everything the call left in the workspace for sequence b.  Run by
+// one wave, by the sequence's last user.
+__device__ void cleanup_wave(const Params& p, int b)
+{
+    const int lane = threadIdx.x & 63;
+    const int G1 = p.gamma + 1;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < 2) reinterpret_cast<uint4*>(p.ctl + b)[lane] = z4;
+    for (int i = lane; i < G1; i += 64) p.cnt1[(int64_t)b * G1 + i] = 0ull;
+    uint4* part = reinterpret_cast<uint4*>(p.part1 + 2 * (size_t)b * G1 * p.nch1);
+    for (int j = lane; j < G1 * p.nch1; j += 64) part[j] = z4;
+    uint4* st = reinterpret_cast<uint4*>(p.stats + (size_t)b * G1);
+    for (int j = lane; j < 2 * G1; j += 64) st[j] = z4;
+    uint4* ss = reinterpret_cast<uint4*>(p.sub + (size_t)b * p.nsub);
+    for (int j = lane; j < 2 * p.nsub; j += 64) ss[j] = z4;
+    if (lane == 0) {
+        const int32_t r = p.rank[b];
+        p.ready[r] = 0;
+        p.rank[b] = 0;
+        if (r == 0) *p.ready_cnt = 0u;
+    }
+}
+
+// The draw of sequence b and its outputs, by one wave, in the launch after
+// every sub-chunk sum is out ([FI] Phase 4: the residual norm(max(0, p_n - q_n)) after a
+// rejection, with [ST]'s fallback to p_n; the bonus row p_gamma after full
+// acceptance).  The exact normaliser S and residual mass Z come from the
+// sub-chunk sums; a scan over the sub-chunk weights in index order finds the
+// sub-chunk holding u * total, and a scan of its 512 elements, with every
+// weight recomputed exactly, finds the token.
+template <int DT, int PT, bool VEC2>
+__device__ void finish_wave(const Params& p, int b)
+{
+    const int lane = threadIdx.x & 63;
+    const int G1 = p.gamma + 1;
+    // everything the outputs need, issued together: lane i <= gamma takes
+    // position i's draft token and row statistics
+    int32_t tok = 0;
+    RowStat st{0.0f, 0, 0.0, 0.0, 0.0};
+    if (lane <= p.gamma) {
+        st = ld_stat(p.stats + (int64_t)b * G1 + lane);
+        if (lane < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + lane];
+    }
+    const uint64_t mask = ld_agent(&p.ctl[b].mask);
+    const double ug = (double)p.uniforms[(int64_t)b * G1 + p.gamma];
+    const SubSum* ss = p.sub + (size_t)b * p.nsub;
+    const int nrounds = (p.nsub + kRound - 1) / kRound;
+    double rE[8], rEA[8], rQA[8];
+    auto load_round = [&](int r) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = r * kRound + lane * 8 + i;
+            if (j < p.nsub) {
+                rE[i] = ss[j].E;
+                rEA[i] = ss[j].EA;
+                rQA[i] = ss[j].QA;
+            } else {
+                rE[i] = rEA[i] = rQA[i] = 0.0;
+            }
+        }
+    };
+    load_round(0);
+
+    const bool bad = __ballot(lane < p.gamma && (tok < 0 || tok >= p.V)) != 0;
+    const bool invalid = (mask & kInvalidBit) || bad;
+    const int n = first_reject(mask, p.gamma);
+    const bool resid = n < p.gamma;
+    int t = -1;
+    double Z = NAN;
+    if (!invalid) {
+        // exact normaliser of row n and the residual mass
+        double a = 0.0;
+        for (int r = 0; r < nrounds; ++r) {
+            if (r > 0) load_round(r);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a += rE[i];
+        }
+        const double S = wave_sum(a);
+        const double invS = 1.0 / S;  // p_v = e_v * invS (within an ulp of e_v / S)
+        double zl = 0.0;
+        if (resid) {
+            for (int r = 0; r < nrounds; ++r) {
+                if (nrounds > 1) load_round(r);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) zl += fmax(0.0, rEA[i] * invS - rQA[i]);
+            }
+        }
+        Z = wave_sum(zl);
+        const bool use_resid = resid && Z > kResidEps;
+        const double total = use_resid ? Z : S;
+        const double target = ug * total;
+        auto sub_weight = [&](int i) { return use_resid ? fmax(0.0, rEA[i] * invS - rQA[i]) : rE[i]; };
+
+        // the sub-chunk whose running weight first exceeds the target: lane
+        // totals scanned across the wave, then the crossing lane's entries
+        int js = -1;
+        double carry = 0.0, pre = 0.0;
+        for (int r = 0; r < nrounds && js < 0; ++r) {
+            if (nrounds > 1) load_round(r);
+            double lt = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lt += sub_weight(i);
+            const double incl = wave_incl_scan(lt);
+            double excl = __shfl_up(incl, 1, 64);
+            if (lane == 0) excl = 0.0;
+            const int L = first_lane(__ballot(lt > 0.0 && carry + incl > target));
+            if (L >= 0) {
+                int found = -1, ipos = -1;
+                double c = carry + excl, cpos = c;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const double w = sub_weight(i);
+                    if (found < 0 && w > 0.0) {
+                        if (c + w > target) found = i;
+                        else { ipos = i; cpos = c; c += w; }
+                    }
+                }
+                if (found < 0) { found = ipos; c = cpos; }  // rounding: the lane's last positive entry
+                const int f = __shfl(found, L, 64);
+                pre = __shfl(c, L, 64);
+                js = r * kRound + L * 8 + f;
+            } else {
+                carry += __shfl(incl, 63, 64);
+            }
+        }
+
+        // scan sub-chunk js (and, only if rounding pushed the crossing out of
+        // it, the sub-chunks after it) in index order, every weight exact
+        const int64_t row = (int64_t)b * G1 + n;
+        const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+        const void* qrow = static_cast<const char*>(p.probs) +
+                           (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
+        const double nMcd = -(double)__shfl(st.m, n, 64) * p.cd;  // lane n holds row n's statistics
+        double rem = target - pre;
+        for (int s = js; js >= 0 && s < p.nsub && t < 0; ++s) {
+            const int idx = s * kSub + lane * 8;
+            if (s * kSub >= p.V) break;
+            const Raw8 zr = load_group<DT, VEC2>(zrow, idx, p.V);
+            Raw8 qr{};
+            if (use_resid) qr = load_group<PT, VEC2>(qrow, idx, p.V);
+            double w[8], lt = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                w[e] = idx + e < p.V ? draw_weight(p, use_resid, raw8_elem<DT>(zr, e),
+                                                   use_resid ? raw8_elem<PT>(qr, e) : 0.0f, nMcd, invS)
+                                     : 0.0;
+                lt += w[e];
+            }
+            const double incl = wave_incl_scan(lt);
+            double excl = __shfl_up(incl, 1, 64);
+            if (lane == 0) excl = 0.0;
+            const int L = first_lane(__ballot(lt > 0.0 && incl > rem));
+            if (L >= 0) {
+                int found = -1, ipos = -1;
+                double c = excl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (found < 0 && w[e] > 0.0) {
+                        if (c + w[e] > rem) found = e;
+                        else { ipos = e; c += w[e]; }
+                    }
+                }
+                if (found < 0) found = ipos;
+                t = s * kSub + L * 8 + __shfl(found, L, 64);
+            } else {
+                rem -= __shfl(incl, 63, 64);
+            }
+        }
+        if (t < 0) {
+            // u * total at or past the end (only by rounding, u < 1): the
+            // largest index with positive weight, searched backwards from the
+            // last sub-chunk whose sum is positive
+            int jl = -1;
+            for (int r = 0; r < nrounds; ++r) {
+                if (nrounds > 1) load_round(r);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (sub_weight(i) > 0.0) jl = r * kRound + lane * 8 + i;
+            }
+            jl = wave_max_i(jl);
+            auto scan_back = [&](int from, bool wres) {
+                for (int s = from; s >= 0; --s) {
+                    if (s * kSub >= p.V) continue;
+                    const int idx = s * kSub + lane * 8;
+                    const Raw8 zr = load_group<DT, VEC2>(zrow, idx, p.V);
+                    Raw8 qr{};
+                    if (wres) qr = load_group<PT, VEC2>(qrow, idx, p.V);
+                    int lastv = -1;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (idx + e < p.V && draw_weight(p, wres, raw8_elem<DT>(zr, e),
+                                                         wres ? raw8_elem<PT>(qr, e) : 0.0f, nMcd, invS) > 0.0)
+                            lastv = idx + e;
+                    lastv = wave_max_i(lastv);
+                    if (lastv >= 0) return lastv;
+                }
+                return -1;
+            };
+            t = scan_back(jl, use_resid);
+            // (the residual support is chosen with the row stage's
+            // normaliser; should no element of it survive the exact one, the
+            // row n itself, which always has an element with e_v = 1)
+            if (t < 0) t = scan_back(p.nsub - 1, false);
+        }
+    }
+
+    // outputs and telemetry
+    if (lane < G1) {
+        int32_t o;
+        if (invalid) o = -1;
+        else if (lane < n) o = tok;
+        else if (lane == n) o = t;
+        else o = -1;
+        p.tok_out[(int64_t)b * G1 + lane] = o;
+        const bool row_seen = !invalid && lane <= n;
+        if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + lane] = row_seen ? st.m : NAN;
+        if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + lane] = row_seen ? st.S : NAN;
+        if (lane < p.gamma) {
+            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + lane] = row_seen ? st.P : NAN;
+            if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + lane] = row_seen ? st.Q : NAN;
+        }
+    }
+    if (lane == 0) {
+        p.n_out[b] = invalid ? -1 : n;
+        if (p.aux_resid) p.aux_resid[b] = (!invalid && resid) ? Z : NAN;
+    }
+    cleanup_wave(p, b);  // every other user of the sequence's workspace is done
+}
+
+// One claimed draw chunk of sequence b, by the whole workgroup: wave w takes
+// sub-chunks c2 * 16 + 4w .. +3.  No workgroup barrier inside.
+template <int DT, int PT, bool VEC2>
+__device__ __forceinline__ void draw_chunk(const Params& p, int b, int c2, uint64_t mask)
+{
+    const int w = threadIdx.x >> 6;
+    draw_wave<DT, PT, VEC2>(p, b, c2 * kSubPerChunk + w * kSubPerWave, mask);
+}
+
+// ------------------------------------------------------------ sample, launch 1
+
+// VMODE: 0 scalar loads everywhere; 1 vector loads in the row stage only;
+// 2 vector loads in the row stage and the draw.
+template <int DT, int PT, int VMODE>
+__global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
+{
+    constexpr bool VEC = VMODE >= 1, VEC2 = VMODE == 2;
     constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
     constexpr int CH = EPT * kThreads;
-    const int c = (int)(blockIdx.x % (unsigned)p.nch);
-    const int t = (int)(blockIdx.x / (unsigned)p.nch);
+    const int c = (int)(blockIdx.x % (unsigned)p.nch1);
+    const int t = (int)(blockIdx.x / (unsigned)p.nch1);
     const int b = t % p.B;
     const int k = t / p.B;
     const int G1 = p.gamma + 1;
     const int64_t row = (int64_t)b * G1 + k;
 
     __shared__ float sm_f[kWaves];
+    __shared__ int sm_i[kWaves];
     __shared__ double sm_d[kWaves];
-    __shared__ int sm_flag;
+    __shared__ int sm_cmd;
+    __shared__ uint64_t sm_mask;
 
-    if (chunk_skipped(p, b, k, &sm_flag)) return;
+    // Row work runs at raised wave priority, draw chunks at the lowest: the
+    // rows sit on the path that decides every sequence's n, the draw chunks
+    // only need to be done by the end of the second launch.
+    __builtin_amdgcn_s_setprio(2);
+    if (k > 0) {
+        // Is this row still needed?  If an earlier position was rejected it
+        // is not; then, once every position up to the first rejection is
+        // decided, claim a draw chunk of the sequence instead.
+        if (threadIdx.x == 0) {
+            int cmd = -2;  // -2: stream the row chunk, -1: nothing, >= 0: draw chunk
+            const uint64_t m = ld_agent(&p.ctl[b].mask);
+            const uint64_t d = ld_agent(&p.ctl[b].dec);
+            const uint64_t cl0 = ld_agent(&p.ctl[b].claim);
+            if ((m & kInvalidBit) || (m & ((1ull << k) - 1ull))) {
+                cmd = -1;
+                const uint64_t all = rows_mask(p.gamma);
+                if (k >= kHelpFrom && (d & all) == all && (uint32_t)cl0 < (uint32_t)p.nch2) {
+                    const uint32_t cl = (uint32_t)add_agent64(&p.ctl[b].claim, 1ull);
+                    // re-read after dec: every reject bit announced by dec is
+                    // in this value
+                    const uint64_t m2 = ld_agent(&p.ctl[b].mask);
+                    if (cl < (uint32_t)p.nch2) { cmd = (int)cl; sm_mask = m2; }
+                }
+            }
+            sm_cmd = cmd;
+        }
+        __syncthreads();
+        const int cmd = sm_cmd;
+        if (cmd != -2) {
+            // (the draw itself waits for the second launch)
+            if (cmd >= 0) {
+                __builtin_amdgcn_s_setprio(0);
+                draw_chunk<DT, PT, VEC2>(p, b, cmd, sm_mask);
+            }
+            return;
+        }
+    }
     // The decision inputs (draft token, its logit and draft probability, the
     // uniform) are fetched while the chunk streams, in case this block turns
     // out to be the row's last.
@@ -561,8 +1043,8 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         xk = p.tokens[(int64_t)b * p.gamma + k];
         uk = p.uniforms[(int64_t)b * G1 + k];
         if (xk >= 0 && xk < p.V) {
-            zx = load_one_rt(p.logits, DT, row * p.V + xk);
-            qx = load_one_rt(p.probs, p.probs_dtype, ((int64_t)b * p.gamma + k) * p.V + xk);
+            zx = load_one<DT>(p.logits, row * p.V + xk);
+            qx = load_one<PT>(p.probs, ((int64_t)b * p.gamma + k) * p.V + xk);
         }
     }
     uint32_t dep = 0;
@@ -573,15 +1055,24 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         ChunkRegs<DT, VEC, EPT> x;
         x.load(rowp, v0, p.V);
 
-        float mx = -INFINITY;
+        auto float_max = [&]() {
+            float m = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < EPT / 8; ++g) {
-            float z[8];
-            x.get8(g, z);
+            for (int g = 0; g < EPT / 8; ++g) {
+                float z[8];
+                x.get8(g, z);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, z[e]);
+                for (int e = 0; e < 8; ++e) m = fmaxf(m, z[e]);
+            }
+            return block_max(m, sm_f);
+        };
+        float mx;
+        if constexpr (DT == SV_BF16 && VEC) {
+            const int hm = block_max_i(x.max_bits16(), sm_i);
+            mx = hm >= 0 ? __uint_as_float((uint32_t)hm << 16) : float_max();
+        } else {
+            mx = float_max();
         }
-        mx = block_max(mx, sm_f);
         x.opaque();
 
         double s = 0.0;
@@ -606,8 +1097,8 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
         if (threadIdx.x >= 64) return;  // only wave 0 goes on (no block barrier below)
         if (threadIdx.x == 0) {
             if (mx > -INFINITY) s *= exp2(-((double)K + mc));
-            const uint64_t w[2] = {(uint64_t)__float_as_uint(mx), (uint64_t)__double_as_longlong(s)};
-            dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
+            const uint64_t w[2] = {(uint64_t)__float_as_uint(mx), dbits(s)};
+            dep = publish(p.part1 + 2 * ((size_t)row * p.nch1 + c), w, p.zero);
             if (k < p.gamma && xk >= 0 && xk < p.V) {
                 evidence = rejection_evidence((double)uk, (double)qx, s, mx, zx, p.cd, p.ex);
                 early_bit = 1ull << k;
@@ -620,14 +1111,14 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
     // Last block of a fully processed row: wave 0 merges the chunk partials.
     const int lane = (int)threadIdx.x;
     float M = -INFINITY;
-    for (int j = lane; j < p.nch; j += 64) {
-        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
+    for (int j = lane; j < p.nch1; j += 64) {
+        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
         M = fmaxf(M, __uint_as_float((uint32_t)ld_agent(slot)));
     }
     M = wave_max(M);
     double S = 0.0;
-    for (int j = lane; j < p.nch; j += 64) {
-        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch + j);
+    for (int j = lane; j < p.nch1; j += 64) {
+        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
         const float mj = __uint_as_float((uint32_t)ld_agent(slot));
         const double sj = __longlong_as_double((long long)ld_agent(slot + 1));
         if (mj > -INFINITY) S += sj * exp2_f64(((double)mj - (double)M) * p.cd, p.ex);
@@ -635,43 +1126,96 @@ __global__ __launch_bounds__(kThreads) void k_rows_sample(const RowParams p)
     S = wave_sum(S);
 
     if (threadIdx.x == 0) {
-        RowStat st;
-        st.m = M;
-        st.amax = -1;
-        st.S = S;
-        st.P = NAN;
-        st.Q = NAN;
+        double P = NAN, Q = NAN;
+        uint64_t maskbits = 0;
         if (k < p.gamma) {
             // [FI] Phase 3 / [PB] section 3: accept x_k iff u_k <= min(1, p/q),
             // q <= 0 accepts ([PB] Reference Implementation).
             if (xk < 0 || xk >= p.V) {
-                __hip_atomic_fetch_or(&p.mask[b], kInvalidBit | (1ull << k), __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+                maskbits = kInvalidBit | (1ull << k);
             } else {
-                const double P = exp2(((double)zx - (double)M) * p.cd) / S;
-                const double Q = (double)qx;
+                P = exp2(((double)zx - (double)M) * p.cd) / S;
+                Q = (double)qx;
                 const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / Q);
-                const double u = (double)uk;
-                st.P = P;
-                st.Q = Q;
-                if (!(u <= thr))
-                    __hip_atomic_fetch_or(&p.mask[b], 1ull << k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!((double)uk <= thr)) maskbits = 1ull << k;
             }
         }
-        p.stats[row] = st;
+        // statistics, then the reject bit, then the decision bit that
+        // announces both (a rejection decides every later position too)
+        const uint64_t w[4] = {stat_word0(M, -1), dbits(S), dbits(P), dbits(Q)};
+        uint64_t dd = publish(reinterpret_cast<uint64_t*>(p.stats + row), w, p.zero);
+        if (maskbits) dd ^= or_agent(&p.ctl[b].mask, maskbits) & p.zero;
+        const uint64_t all = rows_mask(p.gamma);
+        const uint64_t decbits = maskbits ? (all & ~((1ull << k) - 1ull)) : (1ull << k);
+        const uint64_t old = or_agent(&p.ctl[b].dec, decbits | (uint64_t)(fold64(dd) & p.zero));
+        if ((old & all) != all && ((old | decbits) & all) == all) {
+            // n of this sequence just became known: record the order (read
+            // by the second launch)
+            const uint32_t slot = add_agent(p.ready_cnt, 1u);
+            p.ready[slot] = b;
+            p.rank[b] = (int32_t)slot;
+        }
     }
 }
 
-// ----------------------------------------------------------------- row stage, greedy
+// ------------------------------------------------------------ sample, launch 2
+
+// nch2 workgroups per sequence: each takes one draw chunk the first launch
+// left unclaimed, if any.  Workgroup i < B serves the sequence whose n
+// became known (B-1-i)-th, the rest (nch2 - 1 per sequence) follow in the
+// same order, so the sequences resolved last, which have the most
+// unclaimed chunks, are served first.
+template <int DT, int PT, bool VEC2>
+__global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
+{
+    const int i = (int)blockIdx.x;
+    const int r = p.B - 1 - (i < p.B ? i : (i - p.B) / max(p.nch2 - 1, 1));
+    const int b = p.ready[r];
+    __shared__ int sm_cmd;
+    __shared__ uint64_t sm_mask;
+    if (threadIdx.x == 0) {
+        int cmd = -1;
+        if ((uint32_t)ld_agent(&p.ctl[b].claim) < (uint32_t)p.nch2) {
+            const uint32_t cl = (uint32_t)add_agent64(&p.ctl[b].claim, 1ull);
+            if (cl < (uint32_t)p.nch2) cmd = (int)cl;
+        }
+        sm_cmd = cmd;
+        sm_mask = p.ctl[b].mask;  // final: the row stage has finished
+    }
+    __syncthreads();
+    if (sm_cmd >= 0) draw_chunk<DT, PT, VEC2>(p, b, sm_cmd, sm_mask);
+}
+
+// One wave per sequence: the draw, the outputs, and the clearing of the
+// sequence's workspace.
+template <int DT, int PT, bool VEC2>
+__global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
+{
+    const int b = (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+    if (b < p.B) finish_wave<DT, PT, VEC2>(p, b);
+}
+
+// ----------------------------------------------------------------- greedy mode
+
+__device__ __forceinline__ bool greedy_skipped(const Params& p, int b, int k, int* sm_flag)
+{
+    if (k == 0) return false;  // position 0 is always needed (k is uniform)
+    if (threadIdx.x == 0) {
+        const uint64_t m = ld_agent(&p.ctl[b].mask);
+        *sm_flag = ((m & kInvalidBit) | (m & ((1ull << k) - 1ull))) ? 1 : 0;
+    }
+    __syncthreads();
+    return *sm_flag != 0;
+}
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
+__global__ __launch_bounds__(kThreads) void k_rows_greedy(const Params p)
 {
     constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
     constexpr int W = DT == SV_BF16 ? 8 : 4;
     constexpr int CH = EPT * kThreads;
-    const int c = (int)(blockIdx.x % (unsigned)p.nch);
-    const int t = (int)(blockIdx.x / (unsigned)p.nch);
+    const int c = (int)(blockIdx.x % (unsigned)p.nch1);
+    const int t = (int)(blockIdx.x / (unsigned)p.nch1);
     const int b = t % p.B;
     const int k = t / p.B;
     const int G1 = p.gamma + 1;
@@ -681,13 +1225,13 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
     __shared__ int sm_i[kWaves];
     __shared__ int sm_flag;
 
-    if (chunk_skipped(p, b, k, &sm_flag)) return;
+    if (greedy_skipped(p, b, k, &sm_flag)) return;
     // the draft token and its logit, for an early rejection by this chunk
     int xk = -1;
     float zx = 0.0f;
     if (threadIdx.x == 0 && k < p.gamma) {
         xk = p.tokens[(int64_t)b * p.gamma + k];
-        if (xk >= 0 && xk < p.V) zx = load_one_rt(p.logits, DT, row * p.V + xk);
+        if (xk >= 0 && xk < p.V) zx = load_one<DT>(p.logits, row * p.V + xk);
     }
     uint32_t dep = 0;
     {
@@ -706,11 +1250,11 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
         if (threadIdx.x >= 64) return;  // only wave 0 goes on (no block barrier below)
         if (threadIdx.x == 0) {
             const uint64_t w[1] = {((uint64_t)(uint32_t)bi << 32) | (uint64_t)__float_as_uint(bv)};
-            dep = publish(p.part1 + 2 * ((size_t)row * p.nch + c), w, p.zero);
+            dep = publish(p.part1 + 2 * ((size_t)row * p.nch1 + c), w, p.zero);
             // an element of this chunk beats the draft token for the argmax
             // (larger, or equal at a lower index): the position is rejected
             if (k < p.gamma && xk >= 0 && xk < p.V && bi != INT_MAX && (bv > zx || (bv == zx && bi < xk)))
-                __hip_atomic_fetch_or(&p.mask[b], 1ull << k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                or_agent(&p.ctl[b].mask, 1ull << k);
         }
     }
 
@@ -718,8 +1262,8 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
 
     float bv = -INFINITY;
     int bi = INT_MAX;
-    for (int j = (int)threadIdx.x; j < p.nch; j += 64) {
-        const uint64_t w = ld_agent(p.part1 + 2 * ((size_t)row * p.nch + j));
+    for (int j = (int)threadIdx.x; j < p.nch1; j += 64) {
+        const uint64_t w = ld_agent(p.part1 + 2 * ((size_t)row * p.nch1 + j));
         amax_merge(bv, bi, __uint_as_float((uint32_t)w), (int)(uint32_t)(w >> 32));
     }
     wave_amax(bv, bi);
@@ -737,527 +1281,51 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const RowParams p)
             uint64_t bits = 0;
             if (x < 0 || x >= p.V) bits = kInvalidBit | (1ull << k);
             else if (x != bi) bits = 1ull << k;
-            if (bits) __hip_atomic_fetch_or(&p.mask[b], bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (bits) or_agent(&p.ctl[b].mask, bits);
         }
-        p.stats[row] = st;
+        p.stats[row] = st;  // read by the next launch
     }
 }
 
-// ------------------------------------------------------------------- draw stage
-
-struct DrawParams {
-    const void* logits;
-    const void* probs;
-    const int32_t* tokens;
-    const float* uniforms;
-    uint64_t* mask;
-    uint64_t* cnt1;   // row-stage counters and partial slots, cleared per sequence
-    uint64_t* part1;
-    int nch1;
-    RowStat* stats;
-    DrawPart* part2;  // [B][nch2]
-    int32_t* n_out;
-    int32_t* tok_out;
-    double* aux_p;
-    double* aux_q;
-    double* aux_resid;
-    float* aux_rmax;
-    double* aux_rsum;
-    int B, gamma, V, nch2;
-    uint32_t zero;  // always 0 (see publish)
-    double cd;
-    Exp2Coef ex;  // kExp2Coef
-};
-
-// Per-position values the finish of a sequence needs, loaded early by thread
-// i (= position i <= gamma; gamma + 1 <= kThreads): the draft token x_i and
-// the statistics of row i.
-struct PosInfo {
-    int32_t tok;
-    RowStat st;
-};
-__device__ __forceinline__ PosInfo load_pos_info(const DrawParams& p, int b)
+__global__ __launch_bounds__(kThreads) void k_draw_greedy(const Params p)
 {
-    PosInfo pi;
-    pi.tok = 0;
-    pi.st = RowStat{0.0f, 0, 0.0, 0.0, 0.0};
-    const int i = threadIdx.x;
-    if (i <= p.gamma) {
-        pi.st = p.stats[(int64_t)b * (p.gamma + 1) + i];
-        if (i < p.gamma) pi.tok = p.tokens[(int64_t)b * p.gamma + i];
-    }
-    return pi;
-}
-
-// Writes the per-sequence outputs and telemetry, and clears what the call
-// left in the workspace for this sequence.  Called by the whole block.
-__device__ void finish_sequence(const DrawParams& p, int b, int n, int t, bool invalid, double Z, bool sample,
-                                const PosInfo& pi)
-{
-    const int G1 = p.gamma + 1;
-    const int i = threadIdx.x;
-    if (i < G1) {
-        int32_t o;
-        if (invalid) o = -1;
-        else if (i < n) o = pi.tok;
-        else if (i == n) o = t;
-        else o = -1;
-        p.tok_out[(int64_t)b * G1 + i] = o;
-        const RowStat& st = pi.st;
-        p.stats[(int64_t)b * G1 + i] = RowStat{0.0f, 0, 0.0, 0.0, 0.0};  // leave the workspace zero
-        const bool row_seen = !invalid && i <= n;
-        if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + i] = row_seen ? st.m : NAN;
-        if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + i] = (row_seen && sample) ? st.S : NAN;
-        if (i < p.gamma) {
-            const bool tested = sample && row_seen;
-            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + i] = tested ? st.P : NAN;
-            if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + i] = tested ? st.Q : NAN;
-        }
-    }
-    // rows whose chunks were partly skipped kept their arrival count and
-    // partials: clear every row-stage slot of this sequence
-    for (int j = threadIdx.x; j < G1 * p.nch1; j += kThreads) {
-        uint64_t* slot = p.part1 + 2 * ((size_t)b * G1 * p.nch1 + j);
-        st_agent(slot, 0ull);
-        st_agent(slot + 1, 0ull);
-    }
-    for (int i = threadIdx.x; i < G1; i += kThreads)
-        __hip_atomic_store(&p.cnt1[(int64_t)b * G1 + i], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0) {
-        p.n_out[b] = invalid ? -1 : n;
-        if (p.aux_resid) p.aux_resid[b] = (!invalid && sample && n < p.gamma) ? Z : NAN;
-        p.mask[b] = 0ull;
-    }
-}
-
-__device__ __forceinline__ void clear_draw_partials(const DrawParams& p, int b)
-{
-    for (int j = threadIdx.x; j < p.nch2; j += kThreads) p.part2[(size_t)b * p.nch2 + j] = DrawPart{0.0, 0.0, 0.0, 0.0};
-}
-
-// Any draft token of sequence b outside [0, V)?  (Checked over all gamma
-// tokens, also those past the first rejection.)  Called by the whole block.
-__device__ bool tokens_invalid(const DrawParams& p, const PosInfo& pi, int* sm_i)
-{
-    const int i = threadIdx.x;
-    const int bad = (i < p.gamma && (pi.tok < 0 || pi.tok >= p.V)) ? 1 : 0;
-    return block_max_i(bad, sm_i) != 0;
-}
-
-// Loads 8 consecutive elements starting at idx (a multiple of 8 on the
-// vector path).  Past-the-end elements read as `pad`.
-template <int DT, bool VEC, bool FULL>
-__device__ __forceinline__ void load8(const void* rowp, int idx, int V, float pad, float* out)
-{
-    constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
-    if constexpr (VEC) {
-        const int ci = FULL ? idx : min(idx, V - 8);
-        const char* ptr = static_cast<const char*>(rowp) + (size_t)ci * ES;
-        if constexpr (DT == SV_BF16) {
-            const uint4 w = *reinterpret_cast<const uint4*>(ptr);
-            out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x); out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-            out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z); out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
-        } else {
-            const uint4 a = *reinterpret_cast<const uint4*>(ptr);
-            const uint4 b = *reinterpret_cast<const uint4*>(ptr + 16);
-            out[0] = __uint_as_float(a.x); out[1] = __uint_as_float(a.y);
-            out[2] = __uint_as_float(a.z); out[3] = __uint_as_float(a.w);
-            out[4] = __uint_as_float(b.x); out[5] = __uint_as_float(b.y);
-            out[6] = __uint_as_float(b.z); out[7] = __uint_as_float(b.w);
-        }
-        if constexpr (!FULL) {
-            if (idx >= V) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) out[e] = pad;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = idx + e;
-            if constexpr (FULL) {
-                out[e] = load_one<DT>(rowp, i);
-            } else {
-                const float v = load_one<DT>(rowp, min(i, V - 1));
-                out[e] = i < V ? v : pad;
-            }
-        }
-    }
-}
-
-// 8 consecutive elements as raw 128-bit words (one for bf16, two for fp32).
-struct Raw8 {
-    uint4 a, b;
-};
-template <int DT, bool FULL>
-__device__ __forceinline__ Raw8 load_raw8(const void* rowp, int idx, int V)
-{
-    constexpr size_t ES = DT == SV_BF16 ? 2 : 4;
-    const int ci = FULL ? idx : min(idx, V - 8);
-    const char* ptr = static_cast<const char*>(rowp) + (size_t)ci * ES;
-    Raw8 r;
-    r.a = *reinterpret_cast<const uint4*>(ptr);
-    if constexpr (DT == SV_FP32) r.b = *reinterpret_cast<const uint4*>(ptr + 16);
-    else r.b = make_uint4(0u, 0u, 0u, 0u);
-    return r;
-}
-template <int DT>
-__device__ __forceinline__ float raw8_elem(const Raw8& r, int e)
-{
-    if constexpr (DT == SV_BF16) {
-        const uint32_t w = e < 2 ? r.a.x : e < 4 ? r.a.y : e < 6 ? r.a.z : r.a.w;
-        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
-    } else {
-        const uint32_t w = e == 0 ? r.a.x : e == 1 ? r.a.y : e == 2 ? r.a.z : e == 3 ? r.a.w
-                         : e == 4 ? r.b.x : e == 5 ? r.b.y : e == 6 ? r.b.z : r.b.w;
-        return __uint_as_float(w);
-    }
-}
-
-// Chunk sums of the draw stage for this thread's kEpt2 elements: groups of 8
-// consecutive elements at v0 + (g * kThreads + tid) * 8.  Every load of the
-// chunk is issued before the arithmetic starts.
-template <int DT, int PT, bool VEC, bool FULL>
-__device__ __forceinline__ void draw_chunk_sums(const DrawParams& p, const void* zrow, const void* qrow,
-                                                bool resid, int v0, double nMcd, double S_row,
-                                                double& E, double& EA, double& QA)
-{
-    constexpr int NG = kEpt2 / 8;
-    const int tid = (int)threadIdx.x;
-    // e_v = 2^((z - M) log2(e)/T); the shift -M log2(e)/T is rounded once for
-    // the whole row, a common factor that cancels in every ratio used
-    auto element = [&](float zf, float qf) {
-        const double e = exp2_f64(fma((double)zf, p.cd, nMcd), p.ex);
-        E += e;
-        if (resid) {
-            const double qd = (double)qf;
-            const double in = e > qd * S_row ? 1.0 : 0.0;  // in the residual support
-            EA = fma(e, in, EA);
-            QA = fma(qd, in, QA);
-        }
-    };
-    if constexpr (VEC) {
-        Raw8 zr[NG], qr[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) zr[g] = load_raw8<DT, FULL>(zrow, v0 + (g * kThreads + tid) * 8, p.V);
-        if (resid) {
-#pragma unroll
-            for (int g = 0; g < NG; ++g) qr[g] = load_raw8<PT, FULL>(qrow, v0 + (g * kThreads + tid) * 8, p.V);
-        }
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int idx = v0 + (g * kThreads + tid) * 8;
-            if (!FULL && idx >= p.V) continue;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) element(raw8_elem<DT>(zr[g], e), resid ? raw8_elem<PT>(qr[g], e) : 0.0f);
-        }
-    } else {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const int idx = v0 + (g * kThreads + tid) * 8;
-            float z[8], q[8];
-            load8<DT, false, FULL>(zrow, idx, p.V, -INFINITY, z);
-            if (resid) load8<PT, false, FULL>(qrow, idx, p.V, 0.0f, q);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (FULL || idx + e < p.V) element(z[e], resid ? q[e] : 0.0f);
-        }
-    }
-}
-
-// Weight of one element of row n for the inverse-CDF draw: max(0, p - q)
-// with p = e / S, or e itself for the bonus / fallback draw.
-__device__ __forceinline__ double draw_weight(const DrawParams& p, bool use_resid, float z, float q, double nMcd,
-                                              double invS)
-{
-    const double e = exp2_f64(fma((double)z, p.cd, nMcd), p.ex);
-    return use_resid ? fmax(0.0, e * invS - (double)q) : e;
-}
-
-// This thread's share of one draw-stage chunk of row n (and of the draft
-// row): group g holds the 8 elements from base + (g * kThreads + tid) * 8.
-// Vector path: raw 128-bit words, all loads issued together; otherwise
-// unpacked floats.  Elements past V must be ignored by the caller.
-template <int DT, int PT, bool VEC>
-struct ChunkBuf {
-    static constexpr int NG = kEpt2 / 8;
-    Raw8 zr[NG], qr[NG];
-    __device__ __forceinline__ void load(const DrawParams& p, const void* zrow, const void* qrow, bool with_q, int base)
-    {
-        const int tid = (int)threadIdx.x;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) zr[g] = load_raw8<DT, false>(zrow, base + (g * kThreads + tid) * 8, p.V);
-        if (with_q) {
-#pragma unroll
-            for (int g = 0; g < NG; ++g) qr[g] = load_raw8<PT, false>(qrow, base + (g * kThreads + tid) * 8, p.V);
-        }
-    }
-    __device__ __forceinline__ float z(int g, int e) const { return raw8_elem<DT>(zr[g], e); }
-    __device__ __forceinline__ float q(int g, int e) const { return raw8_elem<PT>(qr[g], e); }
-};
-template <int DT, int PT>
-struct ChunkBuf<DT, PT, false> {
-    static constexpr int NG = kEpt2 / 8;
-    float zv[NG][8], qv[NG][8];
-    __device__ __forceinline__ void load(const DrawParams& p, const void* zrow, const void* qrow, bool with_q, int base)
-    {
-        const int tid = (int)threadIdx.x;
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = min(base + (g * kThreads + tid) * 8 + e, p.V - 1);
-                zv[g][e] = load_one<DT>(zrow, i);
-                qv[g][e] = with_q ? load_one<PT>(qrow, i) : 0.0f;
-            }
-    }
-    __device__ __forceinline__ float z(int g, int e) const { return zv[g][e]; }
-    __device__ __forceinline__ float q(int g, int e) const { return qv[g][e]; }
-};
-
-// Where the draw of sequence b reads: n from the reject mask, row n of the
-// target (and of the draft when n < gamma), and the row stage's statistics.
-struct SeqDraw {
-    int n;
-    bool resid;         // n < gamma: residual draw, else bonus draw
-    bool invalid_seen;  // the row stage met an out-of-range draft token
-    const void* zrow;
-    const void* qrow;
-    double nMcd;        // -max_v z * log2(e)/T, rounded once for the row
-    double S_row;       // the row stage's normaliser (fp32 exponentials)
-};
-template <int DT, int PT>
-__device__ __forceinline__ SeqDraw seq_draw(const DrawParams& p, int b)
-{
-    SeqDraw sd;
-    const uint64_t m = p.mask[b];
-    const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
-    sd.invalid_seen = (m & kInvalidBit) != 0;
-    sd.n = rej ? __builtin_ctzll(rej) : p.gamma;
-    sd.resid = sd.n < p.gamma;
-    const int64_t row = (int64_t)b * (p.gamma + 1) + sd.n;
-    const RowStat st = p.stats[row];  // in bounds for any mask (n <= gamma)
-    sd.nMcd = -(double)st.m * p.cd;
-    sd.S_row = st.S;
-    sd.zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
-    sd.qrow = sd.resid ? static_cast<const char*>(p.probs) +
-                             (size_t)((int64_t)b * p.gamma + sd.n) * p.V * (PT == SV_BF16 ? 2 : 4)
-                       : nullptr;
-    return sd;
-}
-
-// Draw stage, first kernel: the chunk sums of row n, one block per (sequence,
-// chunk).  They are consumed by the next kernel, so plain stores suffice.
-template <int DT, int PT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw_sums(const DrawParams p)
-{
-    const int b = (int)(blockIdx.x / (unsigned)p.nch2);
-    const int c = (int)(blockIdx.x % (unsigned)p.nch2);
-    __shared__ double sm_d[kWaves];
-    const SeqDraw sd = seq_draw<DT, PT>(p, b);
-    if (sd.invalid_seen) return;
-    double E = 0.0, EA = 0.0, QA = 0.0;
-    const int v0 = c * kChunk2;
-    // S_row (row stage) only decides which elements lie in the residual
-    // support; the normaliser itself is re-summed in fp64 here.
-    if (v0 + kChunk2 <= p.V)
-        draw_chunk_sums<DT, PT, VEC, true>(p, sd.zrow, sd.qrow, sd.resid, v0, sd.nMcd, sd.S_row, E, EA, QA);
-    else
-        draw_chunk_sums<DT, PT, VEC, false>(p, sd.zrow, sd.qrow, sd.resid, v0, sd.nMcd, sd.S_row, E, EA, QA);
-    E = block_sum(E, sm_d);
-    EA = block_sum(EA, sm_d);
-    QA = block_sum(QA, sm_d);
-    if (threadIdx.x == 0) {
-        DrawPart* slot = p.part2 + (size_t)b * p.nch2 + c;
-        slot->E = E;
-        slot->EA = EA;
-        slot->QA = QA;
-    }
-}
-
-// Draw stage, second kernel: one block per sequence turns the chunk sums into
-// the exact normaliser and residual mass, finds the chunk that holds the
-// inverse-CDF target, scans it for the token and writes the outputs.  (A
-// separate launch spreads these blocks evenly over the XCDs; run by whichever
-// block of a sequence finished last, they piled up on one XCD.)
-template <int DT, int PT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw_finish(const DrawParams p)
-{
-    const int b = blockIdx.x;
-    const int G1 = p.gamma + 1;
-    __shared__ double sm_d[kWaves];
-    __shared__ int sm_i[kWaves];
-    __shared__ double sm_pre;
-    const SeqDraw sd = seq_draw<DT, PT>(p, b);
-    const int n = sd.n;
-    const bool resid = sd.resid;
-    const bool invalid_seen = sd.invalid_seen;
-    const void* zrow = sd.zrow;
-    const void* qrow = sd.qrow;
-    const double nMcd = sd.nMcd;
-
-    // One round trip brings everything the finish needs: the chunk sums
-    // (slot j cached by thread j), the uniform of the draw, and the draft
-    // tokens and row statistics of the outputs.
-    const int tid = (int)threadIdx.x;
-    const PosInfo pi = load_pos_info(p, b);
-    const double ug = (double)p.uniforms[(int64_t)b * G1 + p.gamma];
-    const DrawPart* slots = p.part2 + (size_t)b * p.nch2;
-    double cE = 0.0, cEA = 0.0, cQA = 0.0;
-    if (tid < p.nch2) {
-        cE = slots[tid].E;
-        cEA = slots[tid].EA;
-        cQA = slots[tid].QA;
-    }
-    auto slot3 = [&](int j, double& E, double& EA, double& QA) {
-        if (j == tid) { E = cE; EA = cEA; QA = cQA; return; }
-        E = slots[j].E; EA = slots[j].EA; QA = slots[j].QA;
-    };
-
-    const bool bad_token = tokens_invalid(p, pi, sm_i);  // called by every thread (barriers)
-    const bool invalid = invalid_seen || bad_token;
-    if (invalid) {
-        clear_draw_partials(p, b);
-        finish_sequence(p, b, n, -1, true, NAN, true, pi);
-        return;
-    }
-
-    // exact normaliser of row n and the residual mass, from the chunk sums
-    double S = 0.0;
-    for (int j = tid; j < p.nch2; j += kThreads) {
-        double E, EA, QA;
-        slot3(j, E, EA, QA);
-        S += E;
-    }
-    S = block_sum(S, sm_d);
-    double Z = 0.0;
-    if (resid) {
-        for (int j = tid; j < p.nch2; j += kThreads) {
-            double E, EA, QA;
-            slot3(j, E, EA, QA);
-            Z += fmax(0.0, EA / S - QA);
-        }
-        Z = block_sum(Z, sm_d);
-    }
-    // [FI] Phase 4: residual norm(max(0, p_n - q_n)) after a rejection, with
-    // [ST]'s fallback to p_n; the bonus row p_gamma after full acceptance.
-    const bool use_resid = resid && Z > kResidEps;
-    const double total = use_resid ? Z : S;
-    const double invS = 1.0 / S;  // p_v = e_v * invS (within an ulp of e_v / S)
-    const double target = ug * total;
-    auto chunk_weight = [&](int j) {
-        double E, EA, QA;
-        slot3(j, E, EA, QA);
-        return use_resid ? fmax(0.0, EA / S - QA) : E;
-    };
-
-    // the first chunk whose running weight sum exceeds the target (block scan
-    // over the chunk weights, kThreads chunks per round)
-    int jc = -1;
-    double carry = 0.0;
-    for (int j0 = 0; j0 < p.nch2 && jc < 0; j0 += kThreads) {
-        const int j = j0 + tid;
-        const double w = j < p.nch2 ? chunk_weight(j) : 0.0;
-        double tot;
-        const double excl = block_exclusive_scan(w, sm_d, &tot);
-        const bool hit = j < p.nch2 && w > 0.0 && carry + excl + w > target;
-        const int first = block_min_i(hit ? j : INT_MAX, sm_i);
-        if (first != INT_MAX) {
-            if (j == first) sm_pre = carry + excl;
-            __syncthreads();
-            jc = first;
-            carry = sm_pre;
-            __syncthreads();
-        } else {
-            carry += tot;
-        }
-    }
-    double rem = target - carry;  // target relative to the start of chunk jc
-
-    // scan chunk jc (and, only if rounding pushed the crossing out of it, the
-    // chunks after it) in index order: group g of thread t holds the 8
-    // elements from jc * kChunk2 + (g * kThreads + t) * 8, so the groups are
-    // visited g-major and, within a group, by thread.  The chunk's loads are
-    // all issued before the first group is scanned.
-    int tok = -1;
-    while (jc >= 0 && jc < p.nch2 && tok < 0) {
-        ChunkBuf<DT, PT, VEC> cb;
-        cb.load(p, zrow, qrow, use_resid, jc * kChunk2);
-#pragma unroll
-        for (int g = 0; g < kEpt2 / 8; ++g) {
-            if (tok < 0) {  // uniform
-                const int idx = jc * kChunk2 + (g * kThreads + tid) * 8;
-                double w[8];
-                double local = 0.0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    w[e] = idx + e < p.V ? draw_weight(p, use_resid, cb.z(g, e), use_resid ? cb.q(g, e) : 0.0f, nMcd, invS)
-                                         : 0.0;
-                    local += w[e];
-                }
-                double gtot;
-                const double excl = block_exclusive_scan(local, sm_d, &gtot);
-                int cand = INT_MAX;
-                if (excl + local > rem) {
-                    double cum = excl;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        cum += w[e];
-                        if (cand == INT_MAX && w[e] > 0.0 && cum > rem) cand = idx + e;
-                    }
-                }
-                cand = block_min_i(cand, sm_i);
-                if (cand != INT_MAX) tok = cand;
-                rem -= gtot;
-            }
-        }
-        ++jc;
-    }
-    if (tok < 0) {
-        // u * total at or past the end (only by rounding, u < 1): the largest
-        // index with positive weight, in the last chunk whose weight is > 0
-        int jl = -1;
-        for (int j = tid; j < p.nch2; j += kThreads)
-            if (chunk_weight(j) > 0.0) jl = max(jl, j);
-        jl = block_max_i(jl, sm_i);
-        int lastv = -1;
-        if (jl >= 0) {
-            ChunkBuf<DT, PT, VEC> cb;
-            cb.load(p, zrow, qrow, use_resid, jl * kChunk2);
-#pragma unroll
-            for (int g = 0; g < kEpt2 / 8; ++g) {
-                const int idx = jl * kChunk2 + (g * kThreads + tid) * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (idx + e < p.V &&
-                        draw_weight(p, use_resid, cb.z(g, e), use_resid ? cb.q(g, e) : 0.0f, nMcd, invS) > 0.0)
-                        lastv = max(lastv, idx + e);
-            }
-        }
-        tok = block_max_i(lastv, sm_i);
-    }
-    // every read of this sequence's chunk slots ended before a barrier above
-    clear_draw_partials(p, b);
-    finish_sequence(p, b, n, tok, false, Z, true, pi);
-}
-
-__global__ __launch_bounds__(kThreads) void k_draw_greedy(const DrawParams p)
-{
-    // one block per sequence: n is the first rejected position, the token the
+    // one wave per sequence: n is the first rejected position, the token the
     // argmax of row n ([FI] "Standardized Sampling", argmax case)
     const int b = blockIdx.x;
-    __shared__ int sm_i[kWaves];
-    __shared__ int sm_t;
-    const uint64_t m = p.mask[b];
-    const uint64_t rej = m & ((1ull << p.gamma) - 1ull);
-    const int n = rej ? __builtin_ctzll(rej) : p.gamma;
-    const PosInfo pi = load_pos_info(p, b);
-    if ((int)threadIdx.x == n) sm_t = pi.st.amax;
-    // every thread has read the mask before the barriers in tokens_invalid,
-    // and the mask is cleared only after them (finish_sequence)
-    const bool bad_token = tokens_invalid(p, pi, sm_i);
-    const bool invalid = (m & kInvalidBit) != 0 || bad_token;
-    finish_sequence(p, b, n, invalid ? -1 : sm_t, invalid, NAN, false, pi);
+    if (threadIdx.x >= 64) return;
+    const int lane = threadIdx.x;
+    const int G1 = p.gamma + 1;
+    const uint64_t m = p.ctl[b].mask;
+    const int n = first_reject(m, p.gamma);
+    int32_t tok = 0;
+    RowStat st{0.0f, 0, 0.0, 0.0, 0.0};
+    if (lane <= p.gamma) {
+        st = p.stats[(int64_t)b * G1 + lane];
+        if (lane < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + lane];
+    }
+    const bool bad = __ballot(lane < p.gamma && (tok < 0 || tok >= p.V)) != 0;
+    const bool invalid = (m & kInvalidBit) || bad;
+    const int t = __shfl(st.amax, min(n, 63), 64);
+    if (lane < G1) {
+        int32_t o;
+        if (invalid) o = -1;
+        else if (lane < n) o = tok;
+        else if (lane == n) o = t;
+        else o = -1;
+        p.tok_out[(int64_t)b * G1 + lane] = o;
+        const bool row_seen = !invalid && lane <= n;
+        if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + lane] = row_seen ? st.m : NAN;
+        if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + lane] = NAN;
+        if (lane < p.gamma) {
+            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + lane] = NAN;
+            if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + lane] = NAN;
+        }
+    }
+    if (lane == 0) {
+        p.n_out[b] = invalid ? -1 : n;
+        if (p.aux_resid) p.aux_resid[b] = NAN;
+    }
+    cleanup_wave(p, b);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail)
@@ -1269,37 +1337,48 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 
 // ---------------------------------------------------------------- host dispatch
 
-template <int DT>
-void launch_rows(bool greedy, bool vec, int grid, const RowParams& rp, hipStream_t s)
-{
-    if (greedy) {
-        if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true>), dim3(grid), dim3(kThreads), 0, s, rp);
-        else hipLaunchKernelGGL((k_rows_greedy<DT, false>), dim3(grid), dim3(kThreads), 0, s, rp);
-    } else {
-        if (vec) hipLaunchKernelGGL((k_rows_sample<DT, true>), dim3(grid), dim3(kThreads), 0, s, rp);
-        else hipLaunchKernelGGL((k_rows_sample<DT, false>), dim3(grid), dim3(kThreads), 0, s, rp);
-    }
-}
-
 template <int DT, int PT>
-void launch_draw_sample_t(bool vec, int grid_sums, int grid_finish, const DrawParams& dp, hipStream_t s)
+void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream_t s, hipEvent_t ev_mid,
+                     bool* ok)
 {
-    if (vec) {
-        hipLaunchKernelGGL((k_draw_sums<DT, PT, true>), dim3(grid_sums), dim3(kThreads), 0, s, dp);
-        hipLaunchKernelGGL((k_draw_finish<DT, PT, true>), dim3(grid_finish), dim3(kThreads), 0, s, dp);
-    } else {
-        hipLaunchKernelGGL((k_draw_sums<DT, PT, false>), dim3(grid_sums), dim3(kThreads), 0, s, dp);
-        hipLaunchKernelGGL((k_draw_finish<DT, PT, false>), dim3(grid_finish), dim3(kThreads), 0, s, dp);
+    switch (vmode) {
+    case 2: hipLaunchKernelGGL((k_main_sample<DT, PT, 2>), dim3(grid1), dim3(kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((k_main_sample<DT, PT, 1>), dim3(grid1), dim3(kThreads), 0, s, p); break;
+    default: hipLaunchKernelGGL((k_main_sample<DT, PT, 0>), dim3(grid1), dim3(kThreads), 0, s, p); break;
     }
+    if (hipGetLastError() != hipSuccess) { *ok = false; return; }
+    if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) { *ok = false; return; }
+    const int grid3 = (p.B + kWaves - 1) / kWaves;
+    if (vmode == 2) {
+        hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_finish_sample<DT, PT, true>), dim3(grid3), dim3(kThreads), 0, s, p);
+    } else {
+        hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((k_finish_sample<DT, PT, false>), dim3(grid3), dim3(kThreads), 0, s, p);
+    }
+    if (hipGetLastError() != hipSuccess) *ok = false;
 }
 
-void launch_draw_sample(int dt, int pt, bool vec, int grid_sums, int grid_finish, const DrawParams& dp,
-                        hipStream_t s)
+bool launch_sample(int dt, int pt, int vmode, int grid1, int grid2, const Params& p, hipStream_t s,
+                   hipEvent_t ev_mid)
 {
-    if (dt == SV_FP32 && pt == SV_FP32) launch_draw_sample_t<SV_FP32, SV_FP32>(vec, grid_sums, grid_finish, dp, s);
-    if (dt == SV_FP32 && pt == SV_BF16) launch_draw_sample_t<SV_FP32, SV_BF16>(vec, grid_sums, grid_finish, dp, s);
-    if (dt == SV_BF16 && pt == SV_FP32) launch_draw_sample_t<SV_BF16, SV_FP32>(vec, grid_sums, grid_finish, dp, s);
-    if (dt == SV_BF16 && pt == SV_BF16) launch_draw_sample_t<SV_BF16, SV_BF16>(vec, grid_sums, grid_finish, dp, s);
+    bool ok = true;
+    if (dt == SV_FP32 && pt == SV_FP32) launch_sample_t<SV_FP32, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, &ok);
+    if (dt == SV_FP32 && pt == SV_BF16) launch_sample_t<SV_FP32, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, &ok);
+    if (dt == SV_BF16 && pt == SV_FP32) launch_sample_t<SV_BF16, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, &ok);
+    if (dt == SV_BF16 && pt == SV_BF16) launch_sample_t<SV_BF16, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, &ok);
+    return ok;
+}
+
+template <int DT>
+bool launch_greedy_t(bool vec, int grid1, int B, const Params& p, hipStream_t s, hipEvent_t ev_mid)
+{
+    if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true>), dim3(grid1), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_rows_greedy<DT, false>), dim3(grid1), dim3(kThreads), 0, s, p);
+    if (hipGetLastError() != hipSuccess) return false;
+    if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) return false;
+    hipLaunchKernelGGL(k_draw_greedy, dim3(B), dim3(kThreads), 0, s, p);
+    return hipGetLastError() == hipSuccess;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -1365,14 +1444,13 @@ int spec_verify(int batch, int gamma, int vocab,
     const int chunk1 = logits_dtype == SV_BF16 ? kChunkBf16 : kChunkFp32;
     const int nch1 = (vocab + chunk1 - 1) / chunk1;
     const long long grid1 = (long long)G1 * batch * nch1;
-    if (nch1 > 0xffff || grid1 > INT_MAX) return SV_ERR_TOO_LARGE;
+    const long long grid2 = greedy ? (long long)batch : (long long)batch * L.nch2;
+    if (nch1 > 0xffff || grid1 > INT_MAX || grid2 > INT_MAX) return SV_ERR_TOO_LARGE;
+    // vector loads need 16-byte aligned rows: in the row stage of the logits,
+    // in the draw of the logits and the draft probabilities (8 elements)
     const bool vec = aligned(target_logits, 16) && ((size_t)vocab * lsz) % 16 == 0;
-
-    const int nch2 = (vocab + kChunk2 - 1) / kChunk2;
-    // draw-stage vector loads need 16-byte aligned rows in both tensors
-    const bool vec2 = vocab % 8 == 0 && aligned(target_logits, 16) && (greedy || aligned(draft_probs, 16));
-    const long long grid2 = greedy ? (long long)batch : (long long)batch * nch2;
-    if (grid2 > INT_MAX) return SV_ERR_TOO_LARGE;
+    const bool vec2 = vec && vocab % 8 == 0 && (greedy || aligned(draft_probs, 16));
+    const int vmode = vec2 ? 2 : vec ? 1 : 0;
 
     char* ws = static_cast<char*>(workspace);
     hipStream_t s = (hipStream_t)stream;
@@ -1384,62 +1462,50 @@ int spec_verify(int batch, int gamma, int vocab,
     if ((double)c_hi >= cd) c_hi = std::nextafter(c_hi, 0.0f);
     const float c_lo = (float)(cd - (double)c_hi);
 
-    RowParams rp;
-    rp.logits = target_logits;
-    rp.probs = draft_probs;
-    rp.tokens = draft_tokens;
-    rp.uniforms = uniforms;
-    rp.mask = reinterpret_cast<uint64_t*>(ws + L.mask_off);
-    rp.cnt1 = reinterpret_cast<uint64_t*>(ws + L.cnt1_off);
-    rp.part1 = reinterpret_cast<uint64_t*>(ws + L.part1_off);
-    rp.stats = reinterpret_cast<RowStat*>(ws + L.stats_off);
-    rp.B = batch;
-    rp.gamma = gamma;
-    rp.V = vocab;
-    rp.nch = nch1;
-    rp.probs_dtype = probs_dtype;
-    rp.zero = 0u;
-    rp.c_hi = c_hi;
-    rp.c_lo = c_lo;
-    rp.cd = cd;
-    rp.ex = kExp2Coef;
+    Params p;
+    p.logits = target_logits;
+    p.probs = greedy ? nullptr : draft_probs;
+    p.tokens = draft_tokens;
+    p.uniforms = uniforms;
+    p.ctl = reinterpret_cast<SeqCtl*>(ws + L.ctl_off);
+    p.cnt1 = reinterpret_cast<uint64_t*>(ws + L.cnt1_off);
+    p.part1 = reinterpret_cast<uint64_t*>(ws + L.part1_off);
+    p.stats = reinterpret_cast<RowStat*>(ws + L.stats_off);
+    p.sub = reinterpret_cast<SubSum*>(ws + L.sub_off);
+    p.ready = reinterpret_cast<int32_t*>(ws + L.ready_off);
+    p.rank = reinterpret_cast<int32_t*>(ws + L.rank_off);
+    p.ready_cnt = reinterpret_cast<uint32_t*>(ws + L.rcnt_off);
+    p.n_out = n_accepted;
+    p.tok_out = out_tokens;
+    p.aux_p = extras ? extras->p_tok : nullptr;
+    p.aux_q = extras ? extras->q_tok : nullptr;
+    p.aux_resid = extras ? extras->resid_mass : nullptr;
+    p.aux_rmax = extras ? extras->row_max : nullptr;
+    p.aux_rsum = extras ? extras->row_sum : nullptr;
+    p.B = batch;
+    p.gamma = gamma;
+    p.V = vocab;
+    p.nch1 = nch1;
+    p.nch2 = L.nch2;
+    p.nsub = L.nsub;
+    p.probs_dtype = probs_dtype;
+    p.zero = 0u;
+    p.c_hi = c_hi;
+    p.c_lo = c_lo;
+    p.cd = cd;
+    p.ex = kExp2Coef;
 
-    DrawParams dp;
-    dp.logits = target_logits;
-    dp.probs = draft_probs;
-    dp.tokens = draft_tokens;
-    dp.uniforms = uniforms;
-    dp.mask = rp.mask;
-    dp.cnt1 = rp.cnt1;
-    dp.part1 = rp.part1;
-    dp.nch1 = nch1;
-    dp.stats = rp.stats;
-    dp.part2 = reinterpret_cast<DrawPart*>(ws + L.part2_off);
-    dp.n_out = n_accepted;
-    dp.tok_out = out_tokens;
-    dp.aux_p = extras ? extras->p_tok : nullptr;
-    dp.aux_q = extras ? extras->q_tok : nullptr;
-    dp.aux_resid = extras ? extras->resid_mass : nullptr;
-    dp.aux_rmax = extras ? extras->row_max : nullptr;
-    dp.aux_rsum = extras ? extras->row_sum : nullptr;
-    dp.B = batch;
-    dp.gamma = gamma;
-    dp.V = vocab;
-    dp.nch2 = nch2;
-    dp.zero = 0u;
-    dp.cd = cd;
-    dp.ex = kExp2Coef;
-
+    hipEvent_t ev_mid = extras ? (hipEvent_t)extras->ev_mid : nullptr;
     if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)
         return SV_ERR_LAUNCH;
-    if (logits_dtype == SV_BF16) launch_rows<SV_BF16>(greedy, vec, (int)grid1, rp, s);
-    else launch_rows<SV_FP32>(greedy, vec, (int)grid1, rp, s);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
-    if (extras && extras->ev_mid && hipEventRecord((hipEvent_t)extras->ev_mid, s) != hipSuccess)
-        return SV_ERR_LAUNCH;
-    if (greedy) hipLaunchKernelGGL(k_draw_greedy, dim3((unsigned)grid2), dim3(kThreads), 0, s, dp);
-    else launch_draw_sample(logits_dtype, probs_dtype, vec2, (int)grid2, batch, dp, s);
-    if (hipGetLastError() != hipSuccess) return SV_ERR_LAUNCH;
+    bool ok;
+    if (greedy) {
+        ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)grid1, batch, p, s, ev_mid)
+                                     : launch_greedy_t<SV_FP32>(vec, (int)grid1, batch, p, s, ev_mid);
+    } else {
+        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)grid1, (int)grid2, p, s, ev_mid);
+    }
+    if (!ok) return SV_ERR_LAUNCH;
     if (extras && extras->ev_end && hipEventRecord((hipEvent_t)extras->ev_end, s) != hipSuccess)
         return SV_ERR_LAUNCH;
     return SV_OK;

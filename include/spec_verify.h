@@ -78,9 +78,10 @@ typedef struct {
     float*  row_max;    /* [B][gamma+1] max_v z of each row the walk normalised
                                         (sample) or examined (greedy)            */
     double* row_sum;    /* [B][gamma+1] sum_v exp((z - row_max) / T), sample mode */
-    /* hipEvent_t handles recorded on `stream` around the two kernel stages:
-     * before the row-statistics stage, between the stages, after the draw
-     * stage.  Any may be NULL. */
+    /* hipEvent_t handles recorded on `stream`: before the first launch,
+     * after the first launch (the row stage, which in sample mode also
+     * streams most of the draw), and after the last launch.  Any may be
+     * NULL. */
     void* ev_begin;
     void* ev_mid;
     void* ev_end;
