@@ -79,10 +79,12 @@ constexpr int kChunkBf16 = kEptBf16 * kThreads;  // 16384 elements
 constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
 
 // Draw geometry.  A sub-chunk is 512 consecutive elements of row n, 8 per
-// lane of one wave; a wave takes 4 consecutive sub-chunks and a draw chunk
+// lane of one wave; a wave takes 4 consecutive sub-chunks (in passes of 2,
+// which keeps the fused row kernel at 8 waves per SIMD) and a draw chunk
 // (one claim) is the 4 waves of a workgroup: 8192 elements.
 constexpr int kSub = 512;
 constexpr int kSubPerWave = 4;
+constexpr int kSubPerPass = 2;
 constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16
 constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
 constexpr int kRound = 64 * 8;                      // sub-sums per finish round
@@ -93,6 +95,7 @@ constexpr int kRound = 64 * 8;                      // sub-sums per finish round
 #define SV_HELP_FROM 3
 #endif
 constexpr int kHelpFrom = SV_HELP_FROM;
+
 
 // Per-row statistics written by the row stage.
 struct RowStat {
@@ -575,7 +578,7 @@ struct Params {
     uint64_t* part1;  // [rows][nch1][2]
     RowStat* stats;   // [rows]
     SubSum* sub;      // [B][nsub]
-    int32_t* ready;   // [B] sequences in the order their n became known
+    uint32_t* ready;  // [B] 1 + the sequences, in the order their n became known
     int32_t* rank;    // [B] position of each sequence in `ready`
     uint32_t* ready_cnt;
     int32_t* n_out;
@@ -664,15 +667,15 @@ __device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow
                                                double nMcd, double S_row, double& mE, double& mEA, double& mQA)
 {
     const int lane = threadIdx.x & 63;
-    Raw8 zr[kSubPerWave], qr[kSubPerWave];
+    Raw8 zr[kSubPerPass], qr[kSubPerPass];
 #pragma unroll
-    for (int g = 0; g < kSubPerWave; ++g) zr[g] = load_group<DT, VEC2>(zrow, (s0 + g) * kSub + lane * 8, p.V);
+    for (int g = 0; g < kSubPerPass; ++g) zr[g] = load_group<DT, VEC2>(zrow, (s0 + g) * kSub + lane * 8, p.V);
     if constexpr (RESID) {
 #pragma unroll
-        for (int g = 0; g < kSubPerWave; ++g) qr[g] = load_group<PT, VEC2>(qrow, (s0 + g) * kSub + lane * 8, p.V);
+        for (int g = 0; g < kSubPerPass; ++g) qr[g] = load_group<PT, VEC2>(qrow, (s0 + g) * kSub + lane * 8, p.V);
     }
 #pragma unroll
-    for (int g = 0; g < kSubPerWave; ++g) {
+    for (int g = 0; g < kSubPerPass; ++g) {
         const int idx = (s0 + g) * kSub + lane * 8;
         double E = 0.0, EA = 0.0, QA = 0.0;
 #pragma unroll
@@ -704,27 +707,32 @@ __device__ void draw_wave(const Params& p, int b, int s0, uint64_t mask)
     const int lane = threadIdx.x & 63;
     const int n = first_reject(mask, p.gamma);
     const bool resid = n < p.gamma;
-    double mE = 0.0, mEA = 0.0, mQA = 0.0;  // lane g < 4 keeps sub-chunk s0 + g
+    const int64_t row = (int64_t)b * (p.gamma + 1) + n;
+    double nMcd = 0.0, S_row = 0.0;
     if (!(mask & kInvalidBit)) {
-        const int64_t row = (int64_t)b * (p.gamma + 1) + n;
         const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
-        const uint64_t w0 = ld_agent(sw), w1 = ld_agent(sw + 1);
-        const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
-        const void* qrow = static_cast<const char*>(p.probs) +
-                           (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
-        const double nMcd = -(double)__uint_as_float((uint32_t)w0) * p.cd;
-        const double S_row = __longlong_as_double((long long)w1);
-        const bool full = (s0 + kSubPerWave) * kSub <= p.V;
-        if (resid) {
-            if (full) draw_wave_sums<DT, PT, VEC2, true, true>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
-            else draw_wave_sums<DT, PT, VEC2, true, false>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
-        } else {
-            if (full) draw_wave_sums<DT, PT, VEC2, false, true>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
-            else draw_wave_sums<DT, PT, VEC2, false, false>(p, zrow, qrow, s0, nMcd, S_row, mE, mEA, mQA);
-        }
+        nMcd = -(double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
+        S_row = __longlong_as_double((long long)ld_agent(sw + 1));
     }
-    // lane g < 4 writes sub-chunk s0 + g (read by the finishing launch)
-    if (lane < kSubPerWave) p.sub[(size_t)b * p.nsub + s0 + lane] = SubSum{mE, mEA, mQA, 0.0};
+    const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+    const void* qrow = static_cast<const char*>(p.probs) +
+                       (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
+#pragma unroll
+    for (int s = s0; s < s0 + kSubPerWave; s += kSubPerPass) {
+        double mE = 0.0, mEA = 0.0, mQA = 0.0;  // lane g < kSubPerPass keeps sub-chunk s + g
+        if (!(mask & kInvalidBit)) {
+            const bool full = (s + kSubPerPass) * kSub <= p.V;
+            if (resid) {
+                if (full) draw_wave_sums<DT, PT, VEC2, true, true>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                else draw_wave_sums<DT, PT, VEC2, true, false>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+            } else {
+                if (full) draw_wave_sums<DT, PT, VEC2, false, true>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                else draw_wave_sums<DT, PT, VEC2, false, false>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+            }
+        }
+        // read by the finishing launch
+        if (lane < kSubPerPass) p.sub[(size_t)b * p.nsub + s + lane] = SubSum{mE, mEA, mQA, 0.0};
+    }
 }
 
 // Weight of one element of row n for the inverse-CDF draw: max(0, p - q)
@@ -997,10 +1005,6 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
     __shared__ int sm_cmd;
     __shared__ uint64_t sm_mask;
 
-    // Row work runs at raised wave priority, draw chunks at the lowest: the
-    // rows sit on the path that decides every sequence's n, the draw chunks
-    // only need to be done by the end of the second launch.
-    __builtin_amdgcn_s_setprio(2);
     if (k > 0) {
         // Is this row still needed?  If an earlier position was rejected it
         // is not; then, once every position up to the first rejection is
@@ -1027,10 +1031,7 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
         const int cmd = sm_cmd;
         if (cmd != -2) {
             // (the draw itself waits for the second launch)
-            if (cmd >= 0) {
-                __builtin_amdgcn_s_setprio(0);
-                draw_chunk<DT, PT, VEC2>(p, b, cmd, sm_mask);
-            }
+            if (cmd >= 0) draw_chunk<DT, PT, VEC2>(p, b, cmd, sm_mask);
             return;
         }
     }
@@ -1152,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
             // n of this sequence just became known: record the order (read
             // by the second launch)
             const uint32_t slot = add_agent(p.ready_cnt, 1u);
-            p.ready[slot] = b;
+            __hip_atomic_store(&p.ready[slot], (uint32_t)b + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             p.rank[b] = (int32_t)slot;
         }
     }
@@ -1170,7 +1171,7 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
 {
     const int i = (int)blockIdx.x;
     const int r = p.B - 1 - (i < p.B ? i : (i - p.B) / max(p.nch2 - 1, 1));
-    const int b = p.ready[r];
+    const int b = (int)p.ready[r] - 1;
     __shared__ int sm_cmd;
     __shared__ uint64_t sm_mask;
     if (threadIdx.x == 0) {
@@ -1472,7 +1473,7 @@ int spec_verify(int batch, int gamma, int vocab,
     p.part1 = reinterpret_cast<uint64_t*>(ws + L.part1_off);
     p.stats = reinterpret_cast<RowStat*>(ws + L.stats_off);
     p.sub = reinterpret_cast<SubSum*>(ws + L.sub_off);
-    p.ready = reinterpret_cast<int32_t*>(ws + L.ready_off);
+    p.ready = reinterpret_cast<uint32_t*>(ws + L.ready_off);
     p.rank = reinterpret_cast<int32_t*>(ws + L.rank_off);
     p.ready_cnt = reinterpret_cast<uint32_t*>(ws + L.rcnt_off);
     p.n_out = n_accepted;
