@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified seqs/sec + achieved HBM GB/s (% of peak) at B=256, gamma=8, V=152064"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rows_c4.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_call_c4.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_rejection_sampling_temp_amd", "csrc", "spec_verify.hip")
 
 
@@ -185,7 +185,7 @@ def main():
         with open(KERNEL_SRC, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
         if tr.get("kernel_source_sha256") == sha:
-            traffic = tr.get("hbm_bytes_per_launch")
+            traffic = tr.get("hbm_bytes_per_call")
 
     cpu = None
     if args.cpu_seconds > 0:
