@@ -165,6 +165,10 @@ __device__ __forceinline__ double ld_agent_d(const double* p)
 {
     return __longlong_as_double((long long)ld_agent(reinterpret_cast<const uint64_t*>(p)));
 }
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint64_t xchg_agent(uint64_t* p, uint64_t v)
 {
     return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -617,6 +621,10 @@ __device__ __forceinline__ int first_reject(uint64_t mask, int gamma)
 // fetched sooner; the last block still takes the full decision, which is
 // the same.
 constexpr int kCountBits = 16;
+// merge of a row's partials: slots per lane per pass, and the bound of the
+// wait for a slot whose store is still in flight
+constexpr int kMaxSlotsPerLane = 1;
+constexpr int kSlotPolls = 1 << 20;
 constexpr uint64_t kCountMask = (1ull << kCountBits) - 1ull;
 constexpr double kEvidenceScale = 0x1p30;
 constexpr uint64_t kEvidenceThreshold = (1ull << 30) + (1ull << 14);
@@ -1098,8 +1106,13 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
         if (threadIdx.x >= 64) return;  // only wave 0 goes on (no block barrier below)
         if (threadIdx.x == 0) {
             if (mx > -INFINITY) s *= exp2(-((double)K + mc));
-            const uint64_t w[2] = {(uint64_t)__float_as_uint(mx), dbits(s)};
-            dep = publish(p.part1 + 2 * ((size_t)row * p.nch1 + c), w, p.zero);
+            // the partial goes out with plain device-scope stores and the
+            // count is taken at once; the row's last block waits for every
+            // slot to be filled (a written slot is never all zero: s >= 1
+            // when the max is finite, and -inf has nonzero bits)
+            uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + c);
+            st_agent(slot, (uint64_t)__float_as_uint(mx));
+            st_agent(slot + 1, dbits(s));
             if (k < p.gamma && xk >= 0 && xk < p.V) {
                 evidence = rejection_evidence((double)uk, (double)qx, s, mx, zx, p.cd, p.ex);
                 early_bit = 1ull << k;
@@ -1109,20 +1122,43 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
 
     if (!row_arrive(p, row, b, evidence, early_bit, dep)) return;
 
-    // Last block of a fully processed row: wave 0 merges the chunk partials.
+    // Last block of a fully processed row: wave 0 merges the chunk partials,
+    // once every slot has landed (the stores were issued before the counts).
     const int lane = (int)threadIdx.x;
     float M = -INFINITY;
-    for (int j = lane; j < p.nch1; j += 64) {
-        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
-        M = fmaxf(M, __uint_as_float((uint32_t)ld_agent(slot)));
-    }
-    M = wave_max(M);
     double S = 0.0;
-    for (int j = lane; j < p.nch1; j += 64) {
-        const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
-        const float mj = __uint_as_float((uint32_t)ld_agent(slot));
-        const double sj = __longlong_as_double((long long)ld_agent(slot + 1));
-        if (mj > -INFINITY) S += sj * exp2_f64(((double)mj - (double)M) * p.cd, p.ex);
+    float mj[kMaxSlotsPerLane];
+    double sj[kMaxSlotsPerLane];
+    for (int j0 = 0; j0 < p.nch1; j0 += 64 * kMaxSlotsPerLane) {
+#pragma unroll
+        for (int r = 0; r < kMaxSlotsPerLane; ++r) {
+            const int j = j0 + r * 64 + lane;
+            uint64_t w0 = 0, w1 = 0;
+            if (j < p.nch1) {
+                const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
+                w0 = ld_agent(slot);
+                w1 = ld_agent(slot + 1);
+                for (int it = 0; (w0 | w1) == 0 && it < kSlotPolls; ++it) {
+                    __builtin_amdgcn_s_sleep(1);
+                    w0 = ld_agent(slot);
+                    w1 = ld_agent(slot + 1);
+                }
+            }
+            mj[r] = j < p.nch1 ? __uint_as_float((uint32_t)w0) : -INFINITY;
+            sj[r] = __longlong_as_double((long long)w1);
+        }
+        float mm = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kMaxSlotsPerLane; ++r) mm = fmaxf(mm, mj[r]);
+        mm = wave_max(mm);
+        // rescale what is merged so far to the new maximum
+        if (mm > M) {
+            if (M > -INFINITY) S *= exp2_f64(((double)M - (double)mm) * p.cd, p.ex);
+            M = mm;
+        }
+#pragma unroll
+        for (int r = 0; r < kMaxSlotsPerLane; ++r)
+            if (mj[r] > -INFINITY) S += sj[r] * exp2_f64(((double)mj[r] - (double)M) * p.cd, p.ex);
     }
     S = wave_sum(S);
 
