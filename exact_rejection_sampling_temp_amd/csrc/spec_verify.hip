@@ -121,13 +121,19 @@ struct SeqCtl {
     uint64_t mask;    // bit k: position k rejected; kInvalidBit: a bad draft token
     uint64_t dec;     // bit k: position k decided (a rejection also sets every
                       // later bit); bit gamma: row gamma's statistics out
-    uint64_t claim;   // draw chunks claimed so far
-    uint64_t pad;
+    uint64_t claim;   // low word: draw chunks claimed; high word: claims made
+                      // in the second launch
+    uint64_t cnt2;    // draw wave tasks finished in the second launch, offset
+                      // so that the count reaches kDrawTarget with the last one
+    uint64_t retire;  // low word: users done in the second launch; high word:
+                      // the sequence's rank in the ready list
+    uint64_t pad[3];
 };
-static_assert(sizeof(SeqCtl) == 32, "SeqCtl layout");
+static_assert(sizeof(SeqCtl) == 64, "SeqCtl layout");
+constexpr uint64_t kDrawTarget = 1ull << 40;
 
 struct Layout {
-    size_t ctl_off, cnt1_off, ready_off, rank_off, rcnt_off, control_bytes;
+    size_t ctl_off, cnt1_off, ready_off, rcnt_off, control_bytes;
     size_t part1_off, stats_off, sub_off, total;
     int nch1_max, nch2, nsub;
 };
@@ -145,7 +151,6 @@ Layout make_layout(int B, int gamma, int V)
     L.ctl_off = off;   off = align256(off + sizeof(SeqCtl) * (size_t)B);
     L.cnt1_off = off;  off = align256(off + sizeof(uint64_t) * rows);
     L.ready_off = off; off = align256(off + sizeof(int32_t) * (size_t)B);
-    L.rank_off = off;  off = align256(off + sizeof(int32_t) * (size_t)B);
     L.rcnt_off = off;  off = align256(off + sizeof(uint32_t));
     L.control_bytes = off;
     L.part1_off = off; off = align256(off + 2 * sizeof(uint64_t) * rows * (size_t)L.nch1_max);
@@ -583,7 +588,6 @@ struct Params {
     RowStat* stats;   // [rows]
     SubSum* sub;      // [B][nsub]
     uint32_t* ready;  // [B] 1 + the sequences, in the order their n became known
-    int32_t* rank;    // [B] position of each sequence in `ready`
     uint32_t* ready_cnt;
     int32_t* n_out;
     int32_t* tok_out;
@@ -709,13 +713,18 @@ __device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow
     }
 }
 
-template <int DT, int PT, bool VEC2>
-__device__ void draw_wave(const Params& p, int b, int s0, uint64_t mask)
+// COUNTED (second launch): the sums go out with device-scope exchanges and
+// the wave counts itself in; returns true in the wave that completes the
+// sequence's draw sums.  Otherwise (first launch) plain stores, which the
+// second launch reads after the kernel boundary.
+template <int DT, int PT, bool VEC2, bool COUNTED>
+__device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask)
 {
     const int lane = threadIdx.x & 63;
     const int n = first_reject(mask, p.gamma);
     const bool resid = n < p.gamma;
     const int64_t row = (int64_t)b * (p.gamma + 1) + n;
+    uint64_t dep = 0;
     double nMcd = 0.0, S_row = 0.0;
     if (!(mask & kInvalidBit)) {
         const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
@@ -738,9 +747,23 @@ __device__ void draw_wave(const Params& p, int b, int s0, uint64_t mask)
                 else draw_wave_sums<DT, PT, VEC2, false, false>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
             }
         }
-        // read by the finishing launch
-        if (lane < kSubPerPass) p.sub[(size_t)b * p.nsub + s + lane] = SubSum{mE, mEA, mQA, 0.0};
+        if (lane < kSubPerPass) {
+            if constexpr (COUNTED) {
+                uint64_t* slot = reinterpret_cast<uint64_t*>(p.sub + (size_t)b * p.nsub + s + lane);
+                dep ^= xchg_agent(slot, dbits(mE)) ^ xchg_agent(slot + 1, dbits(mEA)) ^ xchg_agent(slot + 2, dbits(mQA));
+            } else {
+                p.sub[(size_t)b * p.nsub + s + lane] = SubSum{mE, mEA, mQA, 0.0};
+            }
+        }
     }
+    if constexpr (COUNTED) {
+        const uint32_t d = wave_xor(fold64(dep)) & p.zero;
+        uint32_t last = 0;
+        if (lane == 0) last = __hip_atomic_fetch_add(&p.ctl[b].cnt2, 1ull + d, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) + 1ull == kDrawTarget ? 1u : 0u;
+        return __builtin_amdgcn_readfirstlane(last) != 0u;
+    }
+    return false;
 }
 
 // Weight of one element of row n for the inverse-CDF draw: max(0, p - q)
@@ -754,12 +777,12 @@ __device__ __forceinline__ double draw_weight(const Params& p, bool use_resid, f
 
 // Clears everything the call left in the workspace for sequence b.  Run by
 // one wave, by the sequence's last user.
-__device__ void cleanup_wave(const Params& p, int b)
+__device__ void cleanup_wave(const Params& p, int b, uint32_t rank)
 {
     const int lane = threadIdx.x & 63;
     const int G1 = p.gamma + 1;
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < 2) reinterpret_cast<uint4*>(p.ctl + b)[lane] = z4;
+    if (lane < 4) reinterpret_cast<uint4*>(p.ctl + b)[lane] = z4;
     for (int i = lane; i < G1; i += 64) p.cnt1[(int64_t)b * G1 + i] = 0ull;
     uint4* part = reinterpret_cast<uint4*>(p.part1 + 2 * (size_t)b * G1 * p.nch1);
     for (int j = lane; j < G1 * p.nch1; j += 64) part[j] = z4;
@@ -768,15 +791,26 @@ __device__ void cleanup_wave(const Params& p, int b)
     uint4* ss = reinterpret_cast<uint4*>(p.sub + (size_t)b * p.nsub);
     for (int j = lane; j < 2 * p.nsub; j += 64) ss[j] = z4;
     if (lane == 0) {
-        const int32_t r = p.rank[b];
-        p.ready[r] = 0;
-        p.rank[b] = 0;
-        if (r == 0) *p.ready_cnt = 0u;
+        p.ready[rank] = 0u;
+        if (rank == 0) *p.ready_cnt = 0u;
     }
 }
 
-// The draw of sequence b and its outputs, by one wave, in the launch after
-// every sub-chunk sum is out ([FI] Phase 4: the residual norm(max(0, p_n - q_n)) after a
+// Counts one user of sequence b out in the second launch (each of its nch2
+// workgroups, and the draw); the last of the nch2 + 1 clears the sequence.
+// Called by one wave after its reads of the sequence's workspace.
+__device__ __forceinline__ void retire_wave(const Params& p, int b)
+{
+    uint64_t old = 0;
+    if ((threadIdx.x & 63) == 0)
+        old = __hip_atomic_fetch_add(&p.ctl[b].retire, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)old);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(old >> 32));
+    if (lo + 1u == (uint32_t)p.nch2 + 1u) cleanup_wave(p, b, hi);
+}
+
+// The draw of sequence b and its outputs, by one wave, once every
+// sub-chunk sum is out ([FI] Phase 4: the residual norm(max(0, p_n - q_n)) after a
 // rejection, with [ST]'s fallback to p_n; the bonus row p_gamma after full
 // acceptance).  The exact normaliser S and residual mass Z come from the
 // sub-chunk sums; a scan over the sub-chunk weights in index order finds the
@@ -805,9 +839,9 @@ __device__ void finish_wave(const Params& p, int b)
         for (int i = 0; i < 8; ++i) {
             const int j = r * kRound + lane * 8 + i;
             if (j < p.nsub) {
-                rE[i] = ss[j].E;
-                rEA[i] = ss[j].EA;
-                rQA[i] = ss[j].QA;
+                rE[i] = ld_agent_d(&ss[j].E);
+                rEA[i] = ld_agent_d(&ss[j].EA);
+                rQA[i] = ld_agent_d(&ss[j].QA);
             } else {
                 rE[i] = rEA[i] = rQA[i] = 0.0;
             }
@@ -978,16 +1012,16 @@ __device__ void finish_wave(const Params& p, int b)
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = (!invalid && resid) ? Z : NAN;
     }
-    cleanup_wave(p, b);  // every other user of the sequence's workspace is done
 }
 
 // One claimed draw chunk of sequence b, by the whole workgroup: wave w takes
-// sub-chunks c2 * 16 + 4w .. +3.  No workgroup barrier inside.
-template <int DT, int PT, bool VEC2>
-__device__ __forceinline__ void draw_chunk(const Params& p, int b, int c2, uint64_t mask)
+// sub-chunks c2 * 16 + 4w .. +3.  No workgroup barrier inside.  COUNTED:
+// see draw_wave; returns true in the wave that completes the sequence.
+template <int DT, int PT, bool VEC2, bool COUNTED>
+__device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint64_t mask)
 {
     const int w = threadIdx.x >> 6;
-    draw_wave<DT, PT, VEC2>(p, b, c2 * kSubPerChunk + w * kSubPerWave, mask);
+    return draw_wave<DT, PT, VEC2, COUNTED>(p, b, c2 * kSubPerChunk + w * kSubPerWave, mask);
 }
 
 // ------------------------------------------------------------ sample, launch 1
@@ -1039,7 +1073,7 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
         const int cmd = sm_cmd;
         if (cmd != -2) {
             // (the draw itself waits for the second launch)
-            if (cmd >= 0) draw_chunk<DT, PT, VEC2>(p, b, cmd, sm_mask);
+            if (cmd >= 0) draw_chunk<DT, PT, VEC2, false>(p, b, cmd, sm_mask);
             return;
         }
     }
@@ -1190,46 +1224,57 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
             // by the second launch)
             const uint32_t slot = add_agent(p.ready_cnt, 1u);
             __hip_atomic_store(&p.ready[slot], (uint32_t)b + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            p.rank[b] = (int32_t)slot;
+            or_agent(&p.ctl[b].retire, (uint64_t)slot << 32);
         }
     }
 }
 
 // ------------------------------------------------------------ sample, launch 2
 
-// nch2 workgroups per sequence: each takes one draw chunk the first launch
-// left unclaimed, if any.  Workgroup i < B serves the sequence whose n
-// became known (B-1-i)-th, the rest (nch2 - 1 per sequence) follow in the
-// same order, so the sequences resolved last, which have the most
-// unclaimed chunks, are served first.
+// nch2 workgroups per sequence: they take the draw chunks the first launch
+// left, and the wave that completes a sequence's draw sums runs its draw.
+// Workgroup i < B serves the sequence whose n became known (B-1-i)-th, the
+// rest (nch2 - 1 per sequence) follow in the same order: the first claim of
+// every sequence comes early, and the sequences resolved last, which have
+// the most unclaimed chunks, are served first.  A sequence's first claim in
+// this launch learns how many chunks are left (the first launch took the
+// ones before it) and offsets the completion count so that the last of
+// their wave tasks -- or this claim itself, when none is left -- brings it to
+// kDrawTarget.  The last of the sequence's users here clears its workspace.
 template <int DT, int PT, bool VEC2>
 __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
 {
     const int i = (int)blockIdx.x;
     const int r = p.B - 1 - (i < p.B ? i : (i - p.B) / max(p.nch2 - 1, 1));
     const int b = (int)p.ready[r] - 1;
+    if (b < 0 || b >= p.B) return;  // (every sequence is in the list once launch 1 is done)
     __shared__ int sm_cmd;
+    __shared__ int sm_fin;
     __shared__ uint64_t sm_mask;
     if (threadIdx.x == 0) {
-        int cmd = -1;
-        if ((uint32_t)ld_agent(&p.ctl[b].claim) < (uint32_t)p.nch2) {
-            const uint32_t cl = (uint32_t)add_agent64(&p.ctl[b].claim, 1ull);
-            if (cl < (uint32_t)p.nch2) cmd = (int)cl;
+        const uint64_t old = add_agent64(&p.ctl[b].claim, 1ull + (1ull << 32));
+        const uint32_t cl = (uint32_t)old;
+        int fin = 0;
+        if ((old >> 32) == 0) {
+            const uint64_t left = cl < (uint32_t)p.nch2 ? (uint64_t)(p.nch2 - (int)cl) : 0ull;
+            const uint64_t add = kDrawTarget - (uint64_t)kWaves * left;
+            const uint64_t o2 = __hip_atomic_fetch_add(&p.ctl[b].cnt2, add, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            fin = o2 + add == kDrawTarget ? 1 : 0;
         }
-        sm_cmd = cmd;
+        sm_cmd = cl < (uint32_t)p.nch2 ? (int)cl : -1;
+        sm_fin = fin;
         sm_mask = p.ctl[b].mask;  // final: the row stage has finished
     }
     __syncthreads();
-    if (sm_cmd >= 0) draw_chunk<DT, PT, VEC2>(p, b, sm_cmd, sm_mask);
-}
-
-// One wave per sequence: the draw, the outputs, and the clearing of the
-// sequence's workspace.
-template <int DT, int PT, bool VEC2>
-__global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
-{
-    const int b = (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
-    if (b < p.B) finish_wave<DT, PT, VEC2>(p, b);
+    bool fin_wave = sm_fin && threadIdx.x < 64;
+    if (sm_cmd >= 0 && draw_chunk<DT, PT, VEC2, true>(p, b, sm_cmd, sm_mask)) fin_wave = true;
+    if (fin_wave) {
+        finish_wave<DT, PT, VEC2>(p, b);
+        retire_wave(p, b);
+    }
+    __syncthreads();  // this workgroup's work is done
+    if (threadIdx.x < 64) retire_wave(p, b);
 }
 
 // ----------------------------------------------------------------- greedy mode
@@ -1362,7 +1407,7 @@ __global__ __launch_bounds__(kThreads) void k_draw_greedy(const Params p)
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = NAN;
     }
-    cleanup_wave(p, b);
+    cleanup_wave(p, b, 0u);  // (no ready list in greedy mode)
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail)
@@ -1385,14 +1430,8 @@ void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream
     }
     if (hipGetLastError() != hipSuccess) { *ok = false; return; }
     if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) { *ok = false; return; }
-    const int grid3 = (p.B + kWaves - 1) / kWaves;
-    if (vmode == 2) {
-        hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
-        hipLaunchKernelGGL((k_finish_sample<DT, PT, true>), dim3(grid3), dim3(kThreads), 0, s, p);
-    } else {
-        hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
-        hipLaunchKernelGGL((k_finish_sample<DT, PT, false>), dim3(grid3), dim3(kThreads), 0, s, p);
-    }
+    if (vmode == 2) hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
     if (hipGetLastError() != hipSuccess) *ok = false;
 }
 
@@ -1510,7 +1549,6 @@ int spec_verify(int batch, int gamma, int vocab,
     p.stats = reinterpret_cast<RowStat*>(ws + L.stats_off);
     p.sub = reinterpret_cast<SubSum*>(ws + L.sub_off);
     p.ready = reinterpret_cast<uint32_t*>(ws + L.ready_off);
-    p.rank = reinterpret_cast<int32_t*>(ws + L.rank_off);
     p.ready_cnt = reinterpret_cast<uint32_t*>(ws + L.rcnt_off);
     p.n_out = n_accepted;
     p.tok_out = out_tokens;
