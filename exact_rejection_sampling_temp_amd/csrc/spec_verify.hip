@@ -629,6 +629,8 @@ constexpr int kCountBits = 16;
 // wait for a slot whose store is still in flight
 constexpr int kMaxSlotsPerLane = 1;
 constexpr int kSlotPolls = 1 << 20;
+constexpr uint64_t kSlotFlag = 1ull << 32;  // above the max's float bits in a partial's first word
+constexpr uint64_t kSignBit = 1ull << 63;
 constexpr uint64_t kCountMask = (1ull << kCountBits) - 1ull;
 constexpr double kEvidenceScale = 0x1p30;
 constexpr uint64_t kEvidenceThreshold = (1ull << 30) + (1ull << 14);
@@ -1141,12 +1143,14 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
         if (threadIdx.x == 0) {
             if (mx > -INFINITY) s *= exp2(-((double)K + mc));
             // the partial goes out with plain device-scope stores and the
-            // count is taken at once; the row's last block waits for every
-            // slot to be filled (a written slot is never all zero: s >= 1
-            // when the max is finite, and -inf has nonzero bits)
+            // count is taken at once; the row's last block waits until both
+            // words of every slot have landed (neither written word is
+            // zero: the max word carries a flag bit above the float, and
+            // the sum, never negative, goes out with its sign bit flipped;
+            // the two stores may land in either order)
             uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + c);
-            st_agent(slot, (uint64_t)__float_as_uint(mx));
-            st_agent(slot + 1, dbits(s));
+            st_agent(slot, (uint64_t)__float_as_uint(mx) | kSlotFlag);
+            st_agent(slot + 1, dbits(s) ^ kSignBit);
             if (k < p.gamma && xk >= 0 && xk < p.V) {
                 evidence = rejection_evidence((double)uk, (double)qx, s, mx, zx, p.cd, p.ex);
                 early_bit = 1ull << k;
@@ -1172,14 +1176,14 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
                 const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
                 w0 = ld_agent(slot);
                 w1 = ld_agent(slot + 1);
-                for (int it = 0; (w0 | w1) == 0 && it < kSlotPolls; ++it) {
+                for (int it = 0; (w0 == 0 || w1 == 0) && it < kSlotPolls; ++it) {
                     __builtin_amdgcn_s_sleep(1);
                     w0 = ld_agent(slot);
                     w1 = ld_agent(slot + 1);
                 }
             }
             mj[r] = j < p.nch1 ? __uint_as_float((uint32_t)w0) : -INFINITY;
-            sj[r] = __longlong_as_double((long long)w1);
+            sj[r] = __longlong_as_double((long long)(w1 ^ kSignBit));
         }
         float mm = -INFINITY;
 #pragma unroll

@@ -48,6 +48,10 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
                             x["draft_tokens"], x.get("uniforms") if mode == "sample" else None,
                             d.get("temperature", 1.0), mode, aux=aux)
     torch.cuda.synchronize()
+    # every call must leave the shared workspace all zero (the next call may
+    # have another shape, and so another layout of it)
+    for ws in sv._ws_cache.values():
+        assert int(ws.count_nonzero()) == 0, "a finished call must leave the workspace zero"
     res = {"n_accepted": n.cpu().numpy(), "out_tokens": out.cpu().numpy()}
     if aux:
         res.update({k: v.cpu().numpy() for k, v in aux.items()})
