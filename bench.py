@@ -11,9 +11,9 @@ Prints one JSON line: verified sequences/s (value), the roofline of the
 call (achieved algorithmic GB/s from HIP events recorded on the call's stream
 around its launches, against 8 TB/s), and the fp64 CPU oracle timed on this
 host's cores on the same inputs.  The call is one row-stage launch that also
-streams most of the draw (k_main_sample) and two short launches that finish
-the draw (k_rest_sample, k_finish_sample); the row and draw work share the
-first launch, so the roofline covers the whole call.
+streams most of the draw (k_main_sample) and a short launch that finishes
+the draw (k_rest_sample); the row and draw work share the first launch, so
+the roofline covers the whole call.
 """
 from __future__ import annotations
 
@@ -210,11 +210,11 @@ def main():
                    "batch": int(B), "gamma": int(gamma), "vocab": int(V), "input_dtype": "bf16"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "spec_verify call: k_main_sample + k_rest_sample + k_finish_sample",
+                     "kernel": "spec_verify call: k_main_sample + k_rest_sample",
                      "alg_bytes_per_launch": call_alg_bytes, "avg_launch_ms": call_ms},
         "cpu_baseline": cpu,
         "tokens_per_s": tokens_per_s,
-        "stages_ms": {"main": mean_rows_ms, "rest_and_finish": mean_draw_ms},
+        "stages_ms": {"main": mean_rows_ms, "rest": mean_draw_ms},
         "hbm_nominal": {"bytes_per_step": nominal_bytes,
                         "GBps": nominal_bytes / (ms_per_step * 1e-3) / 1e9,
                         "frac": nominal_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},

@@ -11,7 +11,7 @@
 //   [ST] "The exact decoding shortcut that burns compute when guesses miss":
 //        correction_distribution (target row when the residual mass <= 1e-15).
 //
-// Sample mode is three launches on the caller's stream:
+// Sample mode is two launches on the caller's stream:
 //
 //   1. k_main_sample.  The grid enumerates (position k, sequence b, chunk c)
 //      with k slowest.  A workgroup streams one chunk of target row (b, k)
@@ -29,11 +29,9 @@
 //      sums, so the draw of most sequences overlaps the row work of others.
 //
 //   2. k_rest_sample.  Workgroups claim the draw chunks the first launch
-//      left, the sequences resolved last first.
-//
-//   3. k_finish_sample.  One wave per sequence turns the chunk sums into the
-//      inverse-CDF draw, writes the outputs and clears the sequence's
-//      workspace.
+//      left, the sequences resolved last first; the wave that completes a
+//      sequence's sums turns them into the inverse-CDF draw and writes the
+//      outputs, and the sequence's last user clears its workspace.
 //
 // Greedy mode is k_rows_greedy (same grid; chunk argmax) and k_draw_greedy.
 //
