@@ -1026,10 +1026,58 @@ __device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint6
 
 // ------------------------------------------------------------ sample, launch 1
 
+// Decision inputs read through the scalar cache: every lane of the workgroup
+// asks for the same address and the inputs are read-only during the call.
+// The scalar counter is separate from the vector one, so waiting for the
+// control words or the chunk never waits for these, nor the other way round.
+typedef const __attribute__((address_space(4))) uint32_t* ScalarU32;
+
+__device__ __forceinline__ uint32_t scalar_word(const void* p)
+{
+    return *(ScalarU32)p;  // an address-space cast, which only a C-style cast can spell
+}
+
+// The aligned 32-bit word holding element idx (a workgroup-uniform index);
+// word_elem() turns it into the element.  Kept apart so that the wait for the
+// load falls where the value is used, not where it is loaded.
+template <int DT>
+__device__ __forceinline__ uint32_t scalar_elem_word(const void* base, int64_t idx, uint32_t& sel)
+{
+    if constexpr (DT == SV_FP32) {
+        sel = 0;
+        return scalar_word(static_cast<const float*>(base) + idx);
+    } else {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(static_cast<const uint16_t*>(base) + idx);
+        sel = (uint32_t)(a & 2) << 3;  // 16 for the high half
+        return scalar_word(reinterpret_cast<const void*>(a & ~(uintptr_t)3));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float word_elem(uint32_t w, uint32_t sel)
+{
+    if constexpr (DT == SV_FP32) return __uint_as_float(w);
+    else return __uint_as_float((w >> sel) << 16);
+}
+
+// Draft token and uniform of position k of sequence b.
+__device__ __forceinline__ void fetch_token_uniform(const Params& p, int b, int k, int& xk, float& uk)
+{
+    xk = (int)scalar_word(p.tokens + ((int64_t)b * p.gamma + k));
+    uk = __uint_as_float(scalar_word(p.uniforms + ((int64_t)b * (p.gamma + 1) + k)));
+}
+
+// Scalar registers allowed to the first launch's kernel.  Measured on gfx950:
+// a 256-thread workgroup at <= 64 VGPRs gets 8 waves per SIMD only while the
+// kernel descriptor asks for at most ~78 SGPRs (7 at 86, 6 at 100), fewer
+// than the compiler's occupancy model allows, so the cap is explicit (the
+// few values it pushes out live in VGPR lanes).
+constexpr int kMainSgprs = 80;
+
 // VMODE: 0 scalar loads everywhere; 1 vector loads in the row stage only;
 // 2 vector loads in the row stage and the draw.
 template <int DT, int PT, int VMODE>
-__global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs))) void k_main_sample(const Params p)
 {
     constexpr bool VEC = VMODE >= 1, VEC2 = VMODE == 2;
     constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
@@ -1047,6 +1095,15 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
     __shared__ int sm_cmd;
     __shared__ uint64_t sm_mask;
 
+    // The decision inputs (draft token, uniform, then the token's logit and
+    // draft probability) are fetched in case this block turns out to be the
+    // row's last.  The token and uniform go out beside the control words (at
+    // position 0, which has none, behind the chunk's loads); the two loads
+    // that need the token go out behind the chunk's, so no dependent fetch
+    // sits in front of the stream.
+    int xk = 0;
+    float uk = 0.0f;
+    if (k > 0 && k < p.gamma) fetch_token_uniform(p, b, k, xk, uk);
     if (k > 0) {
         // Is this row still needed?  If an earlier position was rejected it
         // is not; then, once every position up to the first rejection is
@@ -1077,19 +1134,7 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
             return;
         }
     }
-    // The decision inputs (draft token, its logit and draft probability, the
-    // uniform) are fetched while the chunk streams, in case this block turns
-    // out to be the row's last.
-    int xk = 0;
-    float zx = 0.0f, qx = 0.0f, uk = 0.0f;
-    if (threadIdx.x == 0 && k < p.gamma) {
-        xk = p.tokens[(int64_t)b * p.gamma + k];
-        uk = p.uniforms[(int64_t)b * G1 + k];
-        if (xk >= 0 && xk < p.V) {
-            zx = load_one<DT>(p.logits, row * p.V + xk);
-            qx = load_one<PT>(p.probs, ((int64_t)b * p.gamma + k) * p.V + xk);
-        }
-    }
+    uint32_t zw = 0, qw = 0, zsel = 0, qsel = 0;
     uint32_t dep = 0;
     uint64_t evidence = 0, early_bit = 0;
     {
@@ -1097,6 +1142,11 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
         const void* rowp = static_cast<const char*>(p.logits) + (size_t)row * (size_t)p.V * (DT == SV_BF16 ? 2 : 4);
         ChunkRegs<DT, VEC, EPT> x;
         x.load(rowp, v0, p.V);
+        if (k == 0 && p.gamma > 0) fetch_token_uniform(p, b, 0, xk, uk);
+        if (k < p.gamma && xk >= 0 && xk < p.V) {
+            zw = scalar_elem_word<DT>(p.logits, row * p.V + xk, zsel);
+            qw = scalar_elem_word<PT>(p.probs, ((int64_t)b * p.gamma + k) * p.V + xk, qsel);
+        }
 
         auto float_max = [&]() {
             float m = -INFINITY;
@@ -1150,7 +1200,8 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
             st_agent(slot, (uint64_t)__float_as_uint(mx) | kSlotFlag);
             st_agent(slot + 1, dbits(s) ^ kSignBit);
             if (k < p.gamma && xk >= 0 && xk < p.V) {
-                evidence = rejection_evidence((double)uk, (double)qx, s, mx, zx, p.cd, p.ex);
+                evidence = rejection_evidence((double)uk, (double)word_elem<PT>(qw, qsel), s, mx,
+                                              word_elem<DT>(zw, zsel), p.cd, p.ex);
                 early_bit = 1ull << k;
             }
         }
@@ -1207,8 +1258,8 @@ __global__ __launch_bounds__(kThreads) void k_main_sample(const Params p)
             if (xk < 0 || xk >= p.V) {
                 maskbits = kInvalidBit | (1ull << k);
             } else {
-                P = exp2(((double)zx - (double)M) * p.cd) / S;
-                Q = (double)qx;
+                P = exp2(((double)word_elem<DT>(zw, zsel) - (double)M) * p.cd) / S;
+                Q = (double)word_elem<PT>(qw, qsel);
                 const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / Q);
                 if (!((double)uk <= thr)) maskbits = 1ull << k;
             }
