@@ -82,7 +82,7 @@ constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
 // (one claim) is the 4 waves of a workgroup: 8192 elements.
 constexpr int kSub = 512;
 constexpr int kSubPerWave = 4;
-constexpr int kSubPerPass = 2;
+constexpr int kSubPerPass = 2;  // first launch (the helpers share SIMDs with the row stage)
 constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16
 constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
 constexpr int kRound = 64 * 8;                      // sub-sums per finish round
@@ -674,20 +674,20 @@ __device__ __forceinline__ bool row_arrive(const Params& p, int64_t row, int b, 
 // decides membership of A; the exact normaliser is the sum of E.  The sums
 // are published to the sub-chunk slots and the wave counts itself in;
 // returns true (wave-uniform) for the last wave task of the sequence.
-template <int DT, int PT, bool VEC2, bool RESID, bool FULL>
+template <int DT, int PT, bool VEC2, bool RESID, bool FULL, int NP>
 __device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow, const void* qrow, int s0,
                                                double nMcd, double S_row, double& mE, double& mEA, double& mQA)
 {
     const int lane = threadIdx.x & 63;
-    Raw8 zr[kSubPerPass], qr[kSubPerPass];
+    Raw8 zr[NP], qr[NP];
 #pragma unroll
-    for (int g = 0; g < kSubPerPass; ++g) zr[g] = load_group<DT, VEC2>(zrow, (s0 + g) * kSub + lane * 8, p.V);
+    for (int g = 0; g < NP; ++g) zr[g] = load_group<DT, VEC2>(zrow, (s0 + g) * kSub + lane * 8, p.V);
     if constexpr (RESID) {
 #pragma unroll
-        for (int g = 0; g < kSubPerPass; ++g) qr[g] = load_group<PT, VEC2>(qrow, (s0 + g) * kSub + lane * 8, p.V);
+        for (int g = 0; g < NP; ++g) qr[g] = load_group<PT, VEC2>(qrow, (s0 + g) * kSub + lane * 8, p.V);
     }
 #pragma unroll
-    for (int g = 0; g < kSubPerPass; ++g) {
+    for (int g = 0; g < NP; ++g) {
         const int idx = (s0 + g) * kSub + lane * 8;
         double E = 0.0, EA = 0.0, QA = 0.0;
 #pragma unroll
@@ -734,20 +734,23 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask)
     const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
     const void* qrow = static_cast<const char*>(p.probs) +
                        (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
+    // the second launch sits on the critical path with SIMDs to spare: all of
+    // a wave's sub-chunks in one load pass there
+    constexpr int NP = COUNTED ? kSubPerWave : kSubPerPass;
 #pragma unroll
-    for (int s = s0; s < s0 + kSubPerWave; s += kSubPerPass) {
-        double mE = 0.0, mEA = 0.0, mQA = 0.0;  // lane g < kSubPerPass keeps sub-chunk s + g
+    for (int s = s0; s < s0 + kSubPerWave; s += NP) {
+        double mE = 0.0, mEA = 0.0, mQA = 0.0;  // lane g < NP keeps sub-chunk s + g
         if (!(mask & kInvalidBit)) {
-            const bool full = (s + kSubPerPass) * kSub <= p.V;
+            const bool full = (s + NP) * kSub <= p.V;
             if (resid) {
-                if (full) draw_wave_sums<DT, PT, VEC2, true, true>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
-                else draw_wave_sums<DT, PT, VEC2, true, false>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                if (full) draw_wave_sums<DT, PT, VEC2, true, true, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                else draw_wave_sums<DT, PT, VEC2, true, false, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
             } else {
-                if (full) draw_wave_sums<DT, PT, VEC2, false, true>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
-                else draw_wave_sums<DT, PT, VEC2, false, false>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                if (full) draw_wave_sums<DT, PT, VEC2, false, true, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                else draw_wave_sums<DT, PT, VEC2, false, false, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
             }
         }
-        if (lane < kSubPerPass) {
+        if (lane < NP) {
             if constexpr (COUNTED) {
                 uint64_t* slot = reinterpret_cast<uint64_t*>(p.sub + (size_t)b * p.nsub + s + lane);
                 dep ^= xchg_agent(slot, dbits(mE)) ^ xchg_agent(slot + 1, dbits(mEA)) ^ xchg_agent(slot + 2, dbits(mQA));
