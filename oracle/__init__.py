@@ -59,6 +59,8 @@ class _Aux(ctypes.Structure):
         ("flag_pos", ctypes.c_void_p),
         ("n_decisions", ctypes.c_void_p),
         ("n_flags", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("alpha", ctypes.c_void_p),
     ]
 
 
@@ -106,7 +108,7 @@ def _ptr(a):
 def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
                     draft_tokens: np.ndarray, uniforms: np.ndarray | None,
                     temperature: float, mode: int = SAMPLE, n_threads: int = 0,
-                    aux: bool = True) -> dict:
+                    aux: bool = True, telemetry: bool = False) -> dict:
     """Run the oracle on host arrays.
 
     target_logits: [B, gamma+1, V] float32 or uint16 (bf16 bits)
@@ -114,7 +116,9 @@ def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
     draft_tokens:  [B, gamma] int32
     uniforms:      [B, gamma+1] float32, or None in greedy mode
     Returns a dict with n_accepted [B], out_tokens [B, gamma+1] and, when
-    ``aux``, the per-decision diagnostics (see spec_verify_ref.c).
+    ``aux``, the per-decision diagnostics (see spec_verify_ref.c); with
+    ``telemetry`` also beta [B, gamma] (sum_v min(p_i, q_i) for every
+    position) and alpha [gamma] (its mean over the batch).
     """
     lib = _load()
     zl = np.ascontiguousarray(target_logits)
@@ -132,6 +136,8 @@ def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
     out = np.empty((B, G1), dtype=np.int32)
     res = {"n_accepted": n_acc, "out_tokens": out}
     aux_s = None
+    if telemetry and not aux:
+        raise ValueError("telemetry outputs come with aux=True")
     if aux:
         arrs = {
             "p_tok": np.empty((B, G), np.float64),
@@ -144,6 +150,9 @@ def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
             "n_decisions": np.empty(B, np.int32),
             "n_flags": np.empty(B, np.int32),
         }
+        if telemetry:
+            arrs["beta"] = np.empty((B, G), np.float64)
+            arrs["alpha"] = np.empty(G, np.float64)
         aux_s = _Aux(**{k: v.ctypes.data for k, v in arrs.items()})
         res.update(arrs)
     rc = lib.spec_verify_ref(

@@ -23,6 +23,9 @@
  *        Algorithm at Position i", and "Reference Implementation".
  *   [ST] "The exact decoding shortcut that burns compute when guesses miss":
  *        the correction_distribution snippet (zero-residual fallback).
+ *   [FI] "Computing alpha from p and q: The DLK Divergence" (Theorem 3.5,
+ *        Corollary 3.6) and "Expected Number of Generated Tokens" (alpha
+ *        as the expectation of beta): the acceptance-rate telemetry.
  *
  * Readings where the pages leave a step open (each one is also listed in the
  * design notes of the repository):
@@ -76,6 +79,8 @@ typedef struct {
     int32_t* flag_pos;    /* [B]          position of the first near-boundary decision, -1    */
     int32_t* n_decisions; /* [B]          acceptance tests run + 1 final draw                 */
     int32_t* n_flags;     /* [B]          near-boundary decisions taken                        */
+    double*  beta;        /* [B][gamma]   sum_v min(p_i, q_i) for EVERY position (sample mode) */
+    double*  alpha;       /* [gamma]      mean over the batch of beta[.][i]                    */
 } ref_aux_t;
 
 /* Exact promotion of one input element to double: fp32 directly, bf16 by
@@ -252,6 +257,23 @@ static void verify_greedy_one(int b, int gamma, int V, const void* zl, int zd,
     if (aux && aux->n_flags) aux->n_flags[b] = 0;
 }
 
+/* Acceptance rate of one position: beta = sum_v min(p(v), q(v)) with p the
+ * temperature softmax of the target row and q the draft row as given
+ * ([FI] Theorem 3.5: the probability that the draft token is accepted,
+ * 1 - DLK(p, q)).  Sequential sum in index order. */
+static double accept_rate_row(const void* zl, int zd, int64_t zoff, const void* qp, int qd,
+                              int64_t qoff, int V, double T, double* p)
+{
+    double m, s;
+    softmax_row(zl, zd, zoff, V, T, p, &m, &s);
+    double beta = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double q = load_elem(qp, qd, qoff + v);
+        beta += p[v] < q ? p[v] : q;
+    }
+    return beta;
+}
+
 static void fill_nan(double* a, int64_t count)
 {
     if (!a) return;
@@ -287,6 +309,8 @@ int spec_verify_ref(int batch, int gamma, int vocab,
         fill_nan(aux->resid_mass, B);
         fill_nan(aux->row_max, B * G1);
         fill_nan(aux->row_sum, B * G1);
+        fill_nan(aux->beta, B * G);
+        fill_nan(aux->alpha, G);
     }
 
 #ifdef _OPENMP
@@ -335,6 +359,40 @@ int spec_verify_ref(int batch, int gamma, int vocab,
         }
         free(p);
         free(w);
+    }
+    if (bad_alloc) return -10;
+
+    /* Telemetry: beta for every position of every sequence (not only the
+     * ones the walk reached), then alpha_i = (1/B) sum_b beta[b][i] summed
+     * in order of b. */
+    if (mode == REF_SAMPLE && aux && (aux->beta || aux->alpha)) {
+        double* beta = aux->beta ? aux->beta : (double*)malloc(sizeof(double) * (size_t)(B * G));
+        if (!beta) return -10;
+#pragma omp parallel num_threads(nt)
+        {
+            double* p = (double*)malloc(sizeof(double) * (size_t)vocab);
+            if (!p) {
+#pragma omp atomic write
+                bad_alloc = 1;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bi = 0; bi < B * G; ++bi) {
+                if (!p) continue;
+                const int64_t b = bi / G, i = bi % G;
+                beta[bi] = accept_rate_row(target_logits, logits_dtype, (b * G1 + i) * vocab,
+                                           draft_probs, probs_dtype, (b * G + i) * vocab, vocab,
+                                           (double)temperature, p);
+            }
+            free(p);
+        }
+        if (aux->alpha && !bad_alloc) {
+            for (int64_t i = 0; i < G; ++i) {
+                double a = 0.0;
+                for (int64_t b = 0; b < B; ++b) a += beta[b * G + i];
+                aux->alpha[i] = a / (double)B;
+            }
+        }
+        if (!aux->beta) free(beta);
     }
     return bad_alloc ? -10 : 0;
 }

@@ -478,3 +478,93 @@ def test_thread_count_does_not_change_results():
                                d["uniforms"], d["temperature"], n_threads=4)
     for k in ("n_accepted", "out_tokens", "p_tok", "resid_mass", "row_sum"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# ------------------------------------------- acceptance-rate telemetry (beta)
+
+def test_beta_is_one_minus_residual_mass():
+    """[FI] Theorem 3.5 with [FI] Phase 4: sum min(p, q) + sum max(0, p - q) =
+    sum p = 1, so at the rejected position the telemetry beta_n and the
+    residual mass the draw used add up to 1 (two separate sums in the oracle)."""
+    d = synth.make_inputs("c2", 3)
+    r = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                               d["uniforms"], d["temperature"], telemetry=True)
+    rej = np.nonzero(r["n_accepted"] < d["gamma"])[0]
+    assert rej.size > 0
+    for b in rej:
+        n = r["n_accepted"][b]
+        assert abs(r["beta"][b, n] + r["resid_mass"][b] - 1.0) < 1e-10
+
+
+def test_beta_matches_dlk_closed_form():
+    """[FI] Definition 3.2 / Lemma 3.3: with M = (p + q)/2, DLK = sum |p - M| =
+    sum |p - q| / 2, and sum min(p, q) = (sum p + sum q - sum |p - q|) / 2 =
+    (1 + sum q)/2 - DLK for a draft row used as given (not renormalised).
+    Every position, reached by the walk or not."""
+    d = synth.make_inputs("c3", 2, B=6)
+    r = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                               d["uniforms"], d["temperature"], telemetry=True)
+    zl = d["target_logits"]
+    q = d["draft_probs"]
+    q64 = q.astype(np.float64) if q.dtype == np.float32 else synth.bf16_bits_to_f32(q).astype(np.float64)
+    for b in range(zl.shape[0]):
+        for i in range(d["gamma"]):
+            p = oracle.softmax_row(zl[b, i], d["temperature"])
+            want = 0.5 * (1.0 + q64[b, i].sum()) - analysis.dlk(p, q64[b, i])
+            assert abs(r["beta"][b, i] - want) < 1e-12
+    assert np.allclose(r["alpha"], r["beta"].mean(axis=0), rtol=0, atol=1e-15)
+
+
+def test_beta_two_token_example():
+    """[ST] two-token example: acceptance is 60 %."""
+    g = _golden("two_token_example.json")
+    zp = np.log(np.array(g["p"])).astype(np.float32)
+    zl = np.stack([zp, zp])[None]
+    q = np.array(g["q"], np.float32)[None, None, :]
+    r = oracle.spec_verify_ref(zl, q, np.array([[1]], np.int32), np.array([[0.5, 0.5]], np.float32),
+                               1.0, telemetry=True)
+    assert abs(r["beta"][0, 0] - g["printed"]["acceptance_rate"]) < 1e-7
+    assert abs(r["alpha"][0] - g["printed"]["acceptance_rate"]) < 1e-7
+
+
+def test_beta_special_cases():
+    """[FI] 'DLK(p,q) = 0 iff p = q' and '= 1 iff disjoint supports': beta is
+    exactly 1 for equal uniform rows and exactly 0 for disjoint supports."""
+    V, gamma = 6, 2
+    zl = np.zeros((2, gamma + 1, V), np.float32)
+    q = np.full((2, gamma, V), 1.0 / V, np.float32)
+    zl[1, :, 3:] = -np.inf
+    q[1] = 0.0
+    q[1, :, 3:] = [0.2, 0.3, 0.5]
+    x = np.array([[0, 1], [4, 5]], np.int32)
+    u = np.full((2, gamma + 1), 0.5, np.float32)
+    r = oracle.spec_verify_ref(zl, q, x, u, 1.0, telemetry=True)
+    p_uniform = oracle.softmax_row(zl[0, 0], 1.0)
+    assert np.all(r["beta"][0] == np.minimum(p_uniform, q[0, 0].astype(np.float64)).sum())
+    assert abs(r["beta"][0, 0] - 1.0) < 1e-7
+    assert np.all(r["beta"][1] == 0.0)
+
+
+def test_beta_is_the_acceptance_probability():
+    """[FI] Theorem 3.5: beta_0 is the probability that the first draft is
+    accepted.  c1 workload (100 000 trials, one fixed row pair per position):
+    the fraction with n >= 1 is Binomial(N, beta_0), checked at 4 sigma; the
+    run-to-run identical rows give identical beta and alpha = beta."""
+    d = synth.make_c1(seed=8, trials=100_000)
+    r = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                               d["uniforms"], d["temperature"], telemetry=True)
+    beta = r["beta"]
+    assert np.all(beta == beta[0])
+    # (alpha sums 100 000 equal terms in order: rounding ~N eps)
+    assert np.allclose(r["alpha"], beta[0], rtol=0, atol=1e-10)
+    b0 = beta[0, 0]
+    N = beta.shape[0]
+    f = float((r["n_accepted"] >= 1).mean())
+    assert abs(f - b0) < 4 * math.sqrt(b0 * (1 - b0) / N), (f, b0)
+    # and position by position: P(n >= j+1 | n >= j) = beta_j
+    n = r["n_accepted"]
+    for j in range(1, d["gamma"]):
+        sel = n >= j
+        fj = float((n[sel] >= j + 1).mean())
+        bj = beta[0, j]
+        assert abs(fj - bj) < 4 * math.sqrt(bj * (1 - bj) / sel.sum()), (j, fj, bj)
