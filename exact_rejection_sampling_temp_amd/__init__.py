@@ -52,6 +52,8 @@ class Extras(ctypes.Structure):
         ("ev_begin", ctypes.c_void_p),
         ("ev_mid", ctypes.c_void_p),
         ("ev_end", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("alpha", ctypes.c_void_p),
     ]
 
 
@@ -126,7 +128,8 @@ def _workspace(device, nbytes: int):
 
 
 _AUX_SPEC = {"p_tok": ("float64", "BG"), "q_tok": ("float64", "BG"), "resid_mass": ("float64", "B"),
-             "row_max": ("float32", "BG1"), "row_sum": ("float64", "BG1")}
+             "row_max": ("float32", "BG1"), "row_sum": ("float64", "BG1"),
+             "beta": ("float64", "BG"), "alpha": ("float64", "G")}
 
 
 def _check_out(t, dtype, numel, dev, name):
@@ -155,7 +158,9 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
 
     ``aux``: optional dict of preallocated device tensors with keys among
     p_tok [B,gamma] f64, q_tok [B,gamma] f64, resid_mass [B] f64,
-    row_max [B,gamma+1] f32, row_sum [B,gamma+1] f64.
+    row_max [B,gamma+1] f32, row_sum [B,gamma+1] f64, and the acceptance-rate
+    telemetry beta [B,gamma] f64 / alpha [gamma] f64 (sample mode; either one
+    makes the call stream every row, see include/spec_verify.h).
     ``events``: optional (begin, mid, end) raw hipEvent_t handles (ints).
     """
     import torch
@@ -194,7 +199,7 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
         if k not in _AUX_SPEC:
             raise ValueError(f"unknown aux output {k!r}")
         dt, per = _AUX_SPEC[k]
-        _check_out(t, getattr(torch, dt), {"B": B, "BG": B * gamma, "BG1": B * G1}[per], dev, k)
+        _check_out(t, getattr(torch, dt), {"B": B, "G": gamma, "BG": B * gamma, "BG1": B * G1}[per], dev, k)
     need = lib.sv_workspace_bytes(B, gamma, V)
     if workspace is None:
         workspace = _workspace(dev, need)

@@ -86,6 +86,8 @@ constexpr int kSubPerPass = 2;  // first launch (the helpers share SIMDs with th
 constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16
 constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
 constexpr int kRound = 64 * 8;                      // sub-sums per finish round
+constexpr int kChunkB = 8192;                       // telemetry sweep: row elements per workgroup
+constexpr int kGroupsB = kChunkB / (8 * kThreads);  // groups of 8 per thread
 // Workgroups of the row stage that find their row unneeded take draw chunks
 // from this position on (earlier positions stream while most of the rows
 // are still needed, and HBM is the shared bottleneck then).
@@ -132,8 +134,8 @@ constexpr uint64_t kDrawTarget = 1ull << 40;
 
 struct Layout {
     size_t ctl_off, cnt1_off, ready_off, rcnt_off, control_bytes;
-    size_t part1_off, stats_off, sub_off, total;
-    int nch1_max, nch2, nsub;
+    size_t part1_off, stats_off, sub_off, bpart_off, total;
+    int nch1_max, nch2, nsub, nchb;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -145,6 +147,7 @@ Layout make_layout(int B, int gamma, int V)
     L.nch1_max = (V + kChunkFp32 - 1) / kChunkFp32;
     L.nch2 = (V + kChunk2 - 1) / kChunk2;
     L.nsub = L.nch2 * kSubPerChunk;
+    L.nchb = (V + kChunkB - 1) / kChunkB;
     size_t off = 0;
     L.ctl_off = off;   off = align256(off + sizeof(SeqCtl) * (size_t)B);
     L.cnt1_off = off;  off = align256(off + sizeof(uint64_t) * rows);
@@ -154,6 +157,7 @@ Layout make_layout(int B, int gamma, int V)
     L.part1_off = off; off = align256(off + 2 * sizeof(uint64_t) * rows * (size_t)L.nch1_max);
     L.stats_off = off; off = align256(off + sizeof(RowStat) * rows);
     L.sub_off = off;   off = align256(off + sizeof(SubSum) * (size_t)B * (size_t)L.nsub);
+    L.bpart_off = off; off = align256(off + sizeof(double) * (size_t)B * (size_t)gamma * (size_t)L.nchb);
     L.total = off;
     return L;
 }
@@ -595,6 +599,10 @@ struct Params {
     float* aux_rmax;
     double* aux_rsum;
     int B, gamma, V, nch1, nch2, nsub, probs_dtype;
+    double* aux_beta;  // telemetry outputs (see sv_extras_t), or NULL
+    double* aux_alpha;
+    double* bpart;     // [B][gamma][nchb] telemetry partial sums
+    int tele, nchb;    // tele: every row is streamed and the telemetry sweep runs
     uint32_t zero;     // always 0 (see publish)
     float c_hi, c_lo;  // log2(e)/T split into two fp32 terms, c_lo > 0
     double cd;         // log2(e)/T in double
@@ -1107,7 +1115,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
     int xk = 0;
     float uk = 0.0f;
     if (k > 0 && k < p.gamma) fetch_token_uniform(p, b, k, xk, uk);
-    if (k > 0) {
+    if (k > 0 && !p.tele) {
         // Is this row still needed?  If an earlier position was rejected it
         // is not; then, once every position up to the first rejection is
         // decided, claim a draw chunk of the sequence instead.
@@ -1283,6 +1291,81 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
             or_agent(&p.ctl[b].retire, (uint64_t)slot << 32);
         }
     }
+}
+
+// ------------------------------------------------------- acceptance telemetry
+
+// beta of position i of sequence b: sum_v min(p_i(v), q_i(v)) ("Fast
+// Inference from Transformers via Speculative Decoding", summary page,
+// Theorem 3.5), swept after the first launch, which in telemetry mode
+// leaves the statistics of every row.  One workgroup per kChunkB elements
+// of row (b, i): p_v = 2^((z_v - m) log2(e)/T) / S with the fp32 exp2 of the
+// row stage (the shift's rounding eta folded into the scale), q_v exact,
+// min and sum in fp64; the workgroup's sum goes to its slot, and
+// k_beta_merge adds a row's slots in index order.
+template <int DT, int PT, bool VEC2>
+__global__ __launch_bounds__(kThreads) void k_beta(const Params p)
+{
+    const int c = (int)(blockIdx.x % (unsigned)p.nchb);
+    const int t = (int)(blockIdx.x / (unsigned)p.nchb);  // b * gamma + i
+    const int b = t / p.gamma;
+    const int i = t - b * p.gamma;
+    const int64_t row = (int64_t)b * (p.gamma + 1) + i;
+    __shared__ double sm_d[kWaves];
+    const int tid = (int)threadIdx.x;
+
+    const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+    const void* qrow = static_cast<const char*>(p.probs) + (size_t)t * p.V * (PT == SV_BF16 ? 2 : 4);
+    Raw8 zr[kGroupsB], qr[kGroupsB];
+#pragma unroll
+    for (int g = 0; g < kGroupsB; ++g) {
+        const int idx = c * kChunkB + (g * kThreads + tid) * 8;
+        zr[g] = load_group<DT, VEC2>(zrow, idx, p.V);
+        qr[g] = load_group<PT, VEC2>(qrow, idx, p.V);
+    }
+    const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
+    const double mc = (double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
+    const double S = __longlong_as_double((long long)ld_agent(sw + 1));
+    const float K = (float)(-mc);
+    const double scale = exp2(-((double)K + mc)) / S;
+
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < kGroupsB; ++g) {
+        const int idx = c * kChunkB + (g * kThreads + tid) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float z = raw8_elem<DT>(zr[g], e);
+            const double pv = (double)__builtin_amdgcn_exp2f(fmaf(z, p.c_lo, fmaf(z, p.c_hi, K))) * scale;
+            const double m = fmin(pv, (double)raw8_elem<PT>(qr[g], e));
+            acc += idx + e < p.V ? m : 0.0;
+        }
+    }
+    const double s = block_sum(acc, sm_d);
+    if (tid == 0) p.bpart[(size_t)t * p.nchb + c] = s;
+}
+
+// beta[b][i] = the row's slots added in index order (and cleared); alpha[i]
+// = the mean over b, with a fixed reduction tree.  One workgroup per
+// position.
+__global__ __launch_bounds__(kThreads) void k_beta_merge(const Params p)
+{
+    const int i = (int)blockIdx.x;
+    __shared__ double sm_d[kWaves];
+    double a = 0.0;
+    for (int b = (int)threadIdx.x; b < p.B; b += kThreads) {
+        double* slot = p.bpart + ((size_t)b * p.gamma + i) * p.nchb;
+        double s = 0.0;
+#pragma unroll 4
+        for (int c = 0; c < p.nchb; ++c) {
+            s += slot[c];
+            slot[c] = 0.0;
+        }
+        if (p.aux_beta) p.aux_beta[(int64_t)b * p.gamma + i] = s;
+        a += s;
+    }
+    a = block_sum(a, sm_d);
+    if (threadIdx.x == 0 && p.aux_alpha) p.aux_alpha[i] = a / (double)p.B;
 }
 
 // ------------------------------------------------------------ sample, launch 2
@@ -1486,6 +1569,13 @@ void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream
     }
     if (hipGetLastError() != hipSuccess) { *ok = false; return; }
     if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) { *ok = false; return; }
+    if (p.tele) {
+        const unsigned gridb = (unsigned)((size_t)p.B * p.gamma * p.nchb);
+        if (vmode == 2) hipLaunchKernelGGL((k_beta<DT, PT, true>), dim3(gridb), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_beta<DT, PT, false>), dim3(gridb), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(k_beta_merge, dim3((unsigned)p.gamma), dim3(kThreads), 0, s, p);
+        if (hipGetLastError() != hipSuccess) { *ok = false; return; }
+    }
     if (vmode == 2) hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
     if (hipGetLastError() != hipSuccess) *ok = false;
@@ -1577,7 +1667,9 @@ int spec_verify(int batch, int gamma, int vocab,
     const int nch1 = (vocab + chunk1 - 1) / chunk1;
     const long long grid1 = (long long)G1 * batch * nch1;
     const long long grid2 = greedy ? (long long)batch : (long long)batch * L.nch2;
-    if (nch1 > 0xffff || grid1 > INT_MAX || grid2 > INT_MAX) return SV_ERR_TOO_LARGE;
+    const bool tele = !greedy && extras && (extras->beta || extras->alpha);
+    const long long gridb = tele ? (long long)batch * gamma * L.nchb : 0;
+    if (nch1 > 0xffff || grid1 > INT_MAX || grid2 > INT_MAX || gridb > INT_MAX) return SV_ERR_TOO_LARGE;
     // vector loads need 16-byte aligned rows: in the row stage of the logits,
     // in the draw of the logits and the draft probabilities (8 elements)
     const bool vec = aligned(target_logits, 16) && ((size_t)vocab * lsz) % 16 == 0;
@@ -1613,6 +1705,11 @@ int spec_verify(int batch, int gamma, int vocab,
     p.aux_resid = extras ? extras->resid_mass : nullptr;
     p.aux_rmax = extras ? extras->row_max : nullptr;
     p.aux_rsum = extras ? extras->row_sum : nullptr;
+    p.aux_beta = tele ? extras->beta : nullptr;
+    p.aux_alpha = tele ? extras->alpha : nullptr;
+    p.bpart = reinterpret_cast<double*>(ws + L.bpart_off);
+    p.tele = tele ? 1 : 0;
+    p.nchb = L.nchb;
     p.B = batch;
     p.gamma = gamma;
     p.V = vocab;

@@ -85,6 +85,21 @@ typedef struct {
     void* ev_begin;
     void* ev_mid;
     void* ev_end;
+    /* Acceptance-rate telemetry, sample mode only ("Fast Inference from
+     * Transformers via Speculative Decoding", paper summary page,
+     * "Computing alpha from p and q: The DLK Divergence", Theorem 3.5: the
+     * probability that the draft at position i is accepted is
+     * beta_i = sum_v min(p_i(v), q_i(v)) = 1 - DLK(p_i, q_i); alpha is its
+     * expectation, "Expected Number of Generated Tokens").  Computed for
+     * EVERY position i < gamma of every sequence, reached by the walk or not
+     * (valid draft tokens or not), with q used as given.  Either pointer
+     * non-NULL makes the call stream every target row and every draft row:
+     * the early exit after a rejection is switched off, and a second sweep
+     * over target rows 0..gamma-1 and the draft rows follows the row stage.
+     * The verification results are the same as without telemetry.  Ignored
+     * in greedy mode. */
+    double* beta;       /* [B][gamma]   beta of position i of sequence b        */
+    double* alpha;      /* [gamma]      mean over the batch of beta[.][i]       */
 } sv_extras_t;
 
 /* Workspace size in bytes for a problem shape (any mode). */

@@ -28,7 +28,7 @@ def to_device(d: dict, device="cuda"):
     return out
 
 
-def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=None):
+def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=None, telemetry: bool = False):
     import torch
     import exact_rejection_sampling_temp_amd as sv
     x = dev_inputs or to_device(d)
@@ -44,6 +44,11 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
             "row_max": torch.empty((B, G1), dtype=torch.float32, device=dv),
             "row_sum": torch.empty((B, G1), dtype=torch.float64, device=dv),
         }
+    if telemetry:
+        dv = x["target_logits"].device
+        aux = aux or {}
+        aux["beta"] = torch.full((B, G), float("nan"), dtype=torch.float64, device=dv)
+        aux["alpha"] = torch.full((G,), float("nan"), dtype=torch.float64, device=dv)
     n, out = sv.spec_verify(x["target_logits"], x.get("draft_probs") if mode == "sample" else None,
                             x["draft_tokens"], x.get("uniforms") if mode == "sample" else None,
                             d.get("temperature", 1.0), mode, aux=aux)
@@ -58,11 +63,11 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
     return res
 
 
-def run_ref(d: dict, mode: str = "sample"):
+def run_ref(d: dict, mode: str = "sample", telemetry: bool = False):
     if mode == "greedy":
         return oracle.spec_verify_ref(d["target_logits"], None, d["draft_tokens"], None, 1.0, oracle.GREEDY)
     return oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
-                                  d["uniforms"], d["temperature"], oracle.SAMPLE)
+                                  d["uniforms"], d["temperature"], oracle.SAMPLE, telemetry=telemetry)
 
 
 def compare(gpu: dict, ref: dict, gamma: int) -> dict:

@@ -1,0 +1,89 @@
+"""GPU parity of the acceptance-rate telemetry: beta[b][i] = sum_v min(p_i, q_i)
+for every position and alpha[i] its batch mean ("Fast Inference from
+Transformers via Speculative Decoding", summary page, Theorem 3.5), against
+the fp64 oracle, through the C ABI (via the binding).
+
+Tolerance: the GPU forms p_v from the row stage's fp32 exp2 (a few ulp,
+~3e-7 relative) scaled by its fp64 normaliser (~1e-8 relative); min and the
+sums are fp64.  Every term's error is at most ~3e-7 of p_v, so |beta_gpu -
+beta_ref| <= 3e-7 * sum_v p_v = 3e-7; the tests allow 1e-6.  Turning the
+telemetry on must not change any verification result.
+"""
+import numpy as np
+import pytest
+
+from tests import synth
+from tests.gpu_util import check_aux, compare, run_gpu, run_ref
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-6
+
+
+def _check_tele(d, with_aux=True):
+    print(f"[telemetry] {d['name']} B={d['B']} gamma={d['gamma']} V={d['V']}", flush=True)
+    g = run_gpu(d, with_aux=with_aux, telemetry=True)
+    r = run_ref(d, telemetry=True)
+    compare(g, r, d["gamma"])
+    if with_aux:
+        check_aux(g, r, 1e-6)
+    assert np.all(np.isfinite(g["beta"])) and np.all(np.isfinite(g["alpha"]))
+    err = np.abs(g["beta"] - r["beta"]).max()
+    assert err < TOL, err
+    assert np.abs(g["alpha"] - r["alpha"]).max() < TOL
+    assert np.all(g["beta"] >= -TOL) and np.all(g["beta"] <= 1 + 2e-3)  # q as given may sum past 1
+    return g, r
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_telemetry_c4_full_size(seed):
+    d = synth.make_inputs("c4", seed)
+    g, r = _check_tele(d)
+    # same verification results as the call without telemetry
+    g0 = run_gpu(d, with_aux=False)
+    assert np.array_equal(g0["n_accepted"], g["n_accepted"])
+    assert np.array_equal(g0["out_tokens"], g["out_tokens"])
+
+
+def test_telemetry_c3_bf16_logits_fp32_probs():
+    _check_tele(synth.make_inputs("c3", 0, B=16))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_telemetry_c2(seed):
+    _check_tele(synth.make_inputs("c2", seed))
+
+
+def test_telemetry_c5_long_gamma():
+    _check_tele(synth.make_inputs("c5", 0, B=8, V=100_000))
+
+
+@pytest.mark.parametrize("V", [7, 1001, 20_001])
+def test_telemetry_scalar_path(V):
+    _check_tele(synth.make_inputs("c2", 40 + V, B=5, V=V))
+
+
+def test_telemetry_covers_invalid_sequences():
+    d = synth.make_inputs("c4", 811, B=6, V=9000)
+    d["draft_tokens"][2, 1] = -1
+    g, r = _check_tele(d)
+    assert g["n_accepted"][2] == -1
+    assert np.abs(g["beta"][2] - r["beta"][2]).max() < TOL
+
+
+def test_telemetry_alpha_only_and_repeated_calls():
+    import torch
+    import exact_rejection_sampling_temp_amd as sv
+    from tests.gpu_util import to_device
+    for name, kw in [("c4", dict(B=8, V=30_000)), ("c2", dict(B=3, V=500)), ("c4", dict(B=8, V=30_000))]:
+        d = synth.make_inputs(name, 820, **kw)
+        x = to_device(d)
+        alpha = torch.full((d["gamma"],), float("nan"), dtype=torch.float64, device="cuda")
+        n, o = sv.spec_verify(x["target_logits"], x["draft_probs"], x["draft_tokens"], x["uniforms"],
+                              d["temperature"], aux={"alpha": alpha})
+        torch.cuda.synchronize()
+        for ws in sv._ws_cache.values():
+            assert int(ws.count_nonzero()) == 0
+        r = run_ref(d, telemetry=True)
+        assert np.abs(alpha.cpu().numpy() - r["alpha"]).max() < TOL
+        assert np.array_equal(n.cpu().numpy(), r["n_accepted"])
