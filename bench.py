@@ -14,6 +14,12 @@ host's cores on the same inputs.  The call is one row-stage launch that also
 streams most of the draw (k_main_sample) and a short launch that finishes
 the draw (k_rest_sample); the row and draw work share the first launch, so
 the roofline covers the whole call.
+
+A second, shorter leg times the same call with the acceptance-rate telemetry
+on (beta for every position, alpha): the row stage then streams every target
+row, and a sweep over target rows 0..gamma-1 and the draft rows (k_beta,
+k_beta_merge) runs before the last launch.  It is reported under
+"telemetry", with the sweep's own roofline.
 """
 from __future__ import annotations
 
@@ -97,6 +103,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=2.0,
                     help="minimum wall time of the CPU-oracle baseline (0 = skip)")
+    ap.add_argument("--tele-steps", type=int, default=40,
+                    help="timed calls with the acceptance-rate telemetry on (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -187,6 +195,51 @@ def main():
         if tr.get("kernel_source_sha256") == sha:
             traffic = tr.get("hbm_bytes_per_call")
 
+    tele = None
+    if args.tele_steps > 0:
+        print("[bench] telemetry leg", file=sys.stderr, flush=True)
+        beta = torch.empty((B, gamma), dtype=torch.float64, device=dev)
+        alpha = torch.empty(gamma, dtype=torch.float64, device=dev)
+
+        def tstep(i, events=None):
+            x = dsets[i % 2]
+            sv.spec_verify(x["target_logits"], x["draft_probs"], x["draft_tokens"], x["uniforms"], T,
+                           "sample", n_accepted=n_acc, out_tokens=outs, workspace=ws, events=events,
+                           stream=stream, aux={"beta": beta, "alpha": alpha})
+
+        for i in range(4):
+            tstep(i)
+        torch.cuda.synchronize()
+        tev = [(hev.create(), hev.create(), hev.create(), hev.create()) for _ in range(args.tele_steps)]
+        t1 = time.perf_counter()
+        for i in range(args.tele_steps):
+            tstep(i, events=tev[i])
+        torch.cuda.synchronize()
+        tel = time.perf_counter() - t1
+        t_main = float(np.mean([hev.elapsed_ms(e[0], e[1]) for e in tev]))
+        t_sweep = float(np.mean([hev.elapsed_ms(e[1], e[3]) for e in tev]))
+        t_rest = float(np.mean([hev.elapsed_ms(e[3], e[2]) for e in tev]))
+        for e in tev:
+            for h in e:
+                hev.destroy(h)
+        # bytes: every target row in the row stage, then target rows
+        # 0..gamma-1 and every draft row in the sweep, then the draw rows
+        main_b = float(B * G1 * V * s_p + B * gamma * (s_p + s_q))
+        sweep_b = float(B * gamma * V * (s_p + s_q))
+        tcall_b = main_b + sweep_b + draw_alg_bytes
+        tcall_ms = 1e3 * tel / args.tele_steps
+        sweep_gbps = sweep_b / (t_sweep * 1e-3) / 1e9
+        tele = {
+            "steps": args.tele_steps, "ms_per_step": tcall_ms, "seqs_per_s": B * args.tele_steps / tel,
+            "stages_ms": {"main_all_rows": t_main, "sweep": t_sweep, "rest": t_rest},
+            "alg_bytes_per_call": tcall_b,
+            "achieved_GBps": tcall_b / ((t_main + t_sweep + t_rest) * 1e-3) / 1e9,
+            "sweep_roofline": {"bound": "hbm", "achieved": sweep_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": sweep_gbps / HBM_PEAK_GBPS, "kernel": "k_beta + k_beta_merge",
+                               "alg_bytes_per_launch": sweep_b, "avg_launch_ms": t_sweep},
+            "alpha": [round(float(a), 6) for a in alpha.cpu().numpy()],
+        }
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -219,6 +272,7 @@ def main():
                         "GBps": nominal_bytes / (ms_per_step * 1e-3) / 1e9,
                         "frac": nominal_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "mean_tokens_per_sequence": float(np.mean([(n + 1).mean() for n in n_sets])),
+        "telemetry": tele,
     }
     print(json.dumps(line), flush=True)
 

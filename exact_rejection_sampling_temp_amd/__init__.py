@@ -54,6 +54,7 @@ class Extras(ctypes.Structure):
         ("ev_end", ctypes.c_void_p),
         ("beta", ctypes.c_void_p),
         ("alpha", ctypes.c_void_p),
+        ("ev_tele", ctypes.c_void_p),
     ]
 
 
@@ -161,7 +162,8 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     row_max [B,gamma+1] f32, row_sum [B,gamma+1] f64, and the acceptance-rate
     telemetry beta [B,gamma] f64 / alpha [gamma] f64 (sample mode; either one
     makes the call stream every row, see include/spec_verify.h).
-    ``events``: optional (begin, mid, end) raw hipEvent_t handles (ints).
+    ``events``: optional (begin, mid, end) or (begin, mid, end, tele) raw
+    hipEvent_t handles (ints); tele is recorded after the telemetry sweep.
     """
     import torch
     lib = load_library()
@@ -210,7 +212,9 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
         for k, t in (aux or {}).items():
             setattr(ex, k, t.data_ptr())
         if events:
-            ex.ev_begin, ex.ev_mid, ex.ev_end = events
+            ex.ev_begin, ex.ev_mid, ex.ev_end = events[:3]
+            if len(events) > 3:
+                ex.ev_tele = events[3]
     rc = lib.spec_verify(
         B, gamma, V,
         target_logits.data_ptr(), _dtype_tag(target_logits),

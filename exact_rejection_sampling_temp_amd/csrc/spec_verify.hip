@@ -88,6 +88,7 @@ constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
 constexpr int kRound = 64 * 8;                      // sub-sums per finish round
 constexpr int kChunkB = 8192;                       // telemetry sweep: row elements per workgroup
 constexpr int kGroupsB = kChunkB / (8 * kThreads);  // groups of 8 per thread
+static_assert(kChunkB == kChunk2, "a telemetry workgroup covers exactly one draw chunk");
 // Workgroups of the row stage that find their row unneeded take draw chunks
 // from this position on (earlier positions stream while most of the rows
 // are still needed, and HBM is the shared bottleneck then).
@@ -1343,6 +1344,16 @@ __global__ __launch_bounds__(kThreads) void k_beta(const Params p)
     }
     const double s = block_sum(acc, sm_d);
     if (tid == 0) p.bpart[(size_t)t * p.nchb + c] = s;
+
+    // The draw of a sequence rejected at position i reads these same two
+    // rows: its draw chunk c (the same span of the row) is summed here and
+    // counted as claimed, so the last launch only finishes the draw.  (The
+    // first launch, which streamed every row, has claimed nothing.)
+    const uint64_t mask = ld_agent(&p.ctl[b].mask);
+    if (!(mask & kInvalidBit) && first_reject(mask, p.gamma) == i) {
+        draw_chunk<DT, PT, VEC2, false>(p, b, c, mask);
+        if (tid == 0) add_agent64(&p.ctl[b].claim, 1ull);
+    }
 }
 
 // beta[b][i] = the row's slots added in index order (and cleared); alpha[i]
@@ -1560,7 +1571,7 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 
 template <int DT, int PT>
 void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream_t s, hipEvent_t ev_mid,
-                     bool* ok)
+                     hipEvent_t ev_tele, bool* ok)
 {
     switch (vmode) {
     case 2: hipLaunchKernelGGL((k_main_sample<DT, PT, 2>), dim3(grid1), dim3(kThreads), 0, s, p); break;
@@ -1575,6 +1586,7 @@ void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream
         else hipLaunchKernelGGL((k_beta<DT, PT, false>), dim3(gridb), dim3(kThreads), 0, s, p);
         hipLaunchKernelGGL(k_beta_merge, dim3((unsigned)p.gamma), dim3(kThreads), 0, s, p);
         if (hipGetLastError() != hipSuccess) { *ok = false; return; }
+        if (ev_tele && hipEventRecord(ev_tele, s) != hipSuccess) { *ok = false; return; }
     }
     if (vmode == 2) hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
@@ -1582,13 +1594,13 @@ void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream
 }
 
 bool launch_sample(int dt, int pt, int vmode, int grid1, int grid2, const Params& p, hipStream_t s,
-                   hipEvent_t ev_mid)
+                   hipEvent_t ev_mid, hipEvent_t ev_tele)
 {
     bool ok = true;
-    if (dt == SV_FP32 && pt == SV_FP32) launch_sample_t<SV_FP32, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, &ok);
-    if (dt == SV_FP32 && pt == SV_BF16) launch_sample_t<SV_FP32, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, &ok);
-    if (dt == SV_BF16 && pt == SV_FP32) launch_sample_t<SV_BF16, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, &ok);
-    if (dt == SV_BF16 && pt == SV_BF16) launch_sample_t<SV_BF16, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, &ok);
+    if (dt == SV_FP32 && pt == SV_FP32) launch_sample_t<SV_FP32, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_FP32 && pt == SV_BF16) launch_sample_t<SV_FP32, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_BF16 && pt == SV_FP32) launch_sample_t<SV_BF16, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_BF16 && pt == SV_BF16) launch_sample_t<SV_BF16, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
     return ok;
 }
 
@@ -1731,7 +1743,8 @@ int spec_verify(int batch, int gamma, int vocab,
         ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)grid1, batch, p, s, ev_mid)
                                      : launch_greedy_t<SV_FP32>(vec, (int)grid1, batch, p, s, ev_mid);
     } else {
-        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)grid1, (int)grid2, p, s, ev_mid);
+        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)grid1, (int)grid2, p, s, ev_mid,
+                           extras ? (hipEvent_t)extras->ev_tele : nullptr);
     }
     if (!ok) return SV_ERR_LAUNCH;
     if (extras && extras->ev_end && hipEventRecord((hipEvent_t)extras->ev_end, s) != hipSuccess)

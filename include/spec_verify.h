@@ -100,6 +100,9 @@ typedef struct {
      * in greedy mode. */
     double* beta;       /* [B][gamma]   beta of position i of sequence b        */
     double* alpha;      /* [gamma]      mean over the batch of beta[.][i]       */
+    /* hipEvent_t recorded after the telemetry sweep (before the last launch)
+     * when the sweep runs; may be NULL. */
+    void* ev_tele;
 } sv_extras_t;
 
 /* Workspace size in bytes for a problem shape (any mode). */
