@@ -78,7 +78,7 @@ def _load():
     lib.spec_verify_ref.argtypes = [
         ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Aux), ctypes.c_int,
     ]
     lib.ref_softmax_row.restype = ctypes.c_int
@@ -108,7 +108,7 @@ def _ptr(a):
 def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
                     draft_tokens: np.ndarray, uniforms: np.ndarray | None,
                     temperature: float, mode: int = SAMPLE, n_threads: int = 0,
-                    aux: bool = True, telemetry: bool = False) -> dict:
+                    aux: bool = True, telemetry: bool = False, lenience: float = 1.0) -> dict:
     """Run the oracle on host arrays.
 
     target_logits: [B, gamma+1, V] float32 or uint16 (bf16 bits)
@@ -118,7 +118,9 @@ def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
     Returns a dict with n_accepted [B], out_tokens [B, gamma+1] and, when
     ``aux``, the per-decision diagnostics (see spec_verify_ref.c); with
     ``telemetry`` also beta [B, gamma] (sum_v min(p_i, q_i) for every
-    position) and alpha [gamma] (its mean over the batch).
+    position) and alpha [gamma] (its mean over the batch).  ``lenience`` l in
+    [0, 1] scales q before the acceptance comparison and in the residual
+    (see spec_verify_ref.c); 1 is the exact method.
     """
     lib = _load()
     zl = np.ascontiguousarray(target_logits)
@@ -158,7 +160,7 @@ def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
     rc = lib.spec_verify_ref(
         B, G, V, _ptr(zl), _dtype_code(zl),
         _ptr(qp), _dtype_code(qp) if qp is not None else 0,
-        _ptr(x), _ptr(u), float(temperature), int(mode),
+        _ptr(x), _ptr(u), float(temperature), float(lenience), int(mode),
         _ptr(n_acc), _ptr(out), ctypes.byref(aux_s) if aux_s is not None else None,
         int(n_threads))
     if rc != 0:

@@ -26,6 +26,10 @@
  *   [FI] "Computing alpha from p and q: The DLK Divergence" (Theorem 3.5,
  *        Corollary 3.6) and "Expected Number of Generated Tokens" (alpha
  *        as the expectation of beta): the acceptance-rate telemetry.
+ *   [FI] "Ablation Studies and Robustness Checks" (Appendix A.5) and "How
+ *        This Work Changes the Landscape": a lenience l in [0, 1] multiplies
+ *        q(x) before it is compared with p(x), and no token is then sampled
+ *        with probability above p(x)/l.
  *
  * Readings where the pages leave a step open (each one is also listed in the
  * design notes of the repository):
@@ -44,7 +48,12 @@
  *     the raw target logits, and the emitted token is that argmax ([FI]
  *     "Standardized Sampling", argmax case);
  *   - a draft token outside [0, V) marks the whole sequence invalid:
- *     n_accepted = -1 and every output token = -1.
+ *     n_accepted = -1 and every output token = -1;
+ *   - lenience l (the pages give only the acceptance side): accept iff
+ *     u <= min(1, p / (l q)), and after a rejection draw from
+ *     norm(max(0, p - l q)), the residual of the same comparison (the same
+ *     [ST] fallback to p when its mass is <= 1e-15); l = 1 is the exact
+ *     method, l = 0 accepts every draft.
  */
 #include <math.h>
 #include <stdint.h>
@@ -171,7 +180,7 @@ static int icdf_draw(const double* w, int V, double u, int* flagged)
  * correction distribution of [FI] Phase 4 / [ST]. */
 static void verify_sample_one(int b, int gamma, int V,
                               const void* zl, int zd, const void* qp, int qd,
-                              const int32_t* x, const float* u, double T,
+                              const int32_t* x, const float* u, double T, double l,
                               int32_t* n_out, int32_t* tok_out,
                               const ref_aux_t* aux, double* p, double* w)
 {
@@ -189,7 +198,8 @@ static void verify_sample_one(int b, int gamma, int V,
         /* Phase 3: accept x_i with probability min(1, p_i(x_i)/q_i(x_i)). */
         double P = p[x[i]];
         double Q = load_elem(qp, qd, ((int64_t)b * gamma + i) * V + x[i]);
-        double thr = (Q <= 0.0) ? 1.0 : fmin(1.0, P / Q);
+        double lQ = l * Q; /* lenience scales q before the comparison (l = 1: exact) */
+        double thr = (Q <= 0.0) ? 1.0 : fmin(1.0, P / lQ);
         double ui = (double)u[i];
         ++n_dec;
         if (near_boundary(ui, thr, REF_NEAR_REL)) { ++n_flag; if (first_flag < 0) first_flag = i; }
@@ -205,10 +215,10 @@ static void verify_sample_one(int b, int gamma, int V,
     double ug = (double)u[gamma];
     if (n < gamma) {
         /* Phase 4, rejection at position n: p holds p_n already.  Sample from
-         * norm(max(0, p_n - q_n)); if that mass is <= 1e-15 use p_n ([ST]). */
+         * norm(max(0, p_n - l q_n)); if that mass is <= 1e-15 use p_n ([ST]). */
         double Z = 0.0;
         for (int v = 0; v < V; ++v) {
-            double r = p[v] - load_elem(qp, qd, ((int64_t)b * gamma + n) * V + v);
+            double r = p[v] - l * load_elem(qp, qd, ((int64_t)b * gamma + n) * V + v);
             w[v] = r > 0.0 ? r : 0.0;
             Z += w[v];
         }
@@ -285,7 +295,7 @@ int spec_verify_ref(int batch, int gamma, int vocab,
                     const void* target_logits, int logits_dtype,
                     const void* draft_probs, int probs_dtype,
                     const int32_t* draft_tokens, const float* uniforms,
-                    float temperature, int mode,
+                    float temperature, float lenience, int mode,
                     int32_t* n_accepted, int32_t* out_tokens,
                     const ref_aux_t* aux, int n_threads)
 {
@@ -299,6 +309,7 @@ int spec_verify_ref(int batch, int gamma, int vocab,
         if (!draft_probs || !uniforms) return -1;
         if (probs_dtype != REF_FP32 && probs_dtype != REF_BF16) return -6;
         if (!(temperature > 0.0f) || !isfinite(temperature)) return -5;
+        if (!(lenience >= 0.0f && lenience <= 1.0f)) return -12;
     }
 
     const int64_t B = batch, G = gamma, G1 = gamma + 1;
@@ -354,7 +365,7 @@ int spec_verify_ref(int batch, int gamma, int vocab,
             } else if (p && w) {
                 verify_sample_one((int)b, gamma, vocab, target_logits, logits_dtype,
                                   draft_probs, probs_dtype, x, uniforms + b * G1,
-                                  (double)temperature, &n_accepted[b], tok, aux, p, w);
+                                  (double)temperature, (double)lenience, &n_accepted[b], tok, aux, p, w);
             }
         }
         free(p);

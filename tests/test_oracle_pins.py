@@ -568,3 +568,69 @@ def test_beta_is_the_acceptance_probability():
         fj = float((n[sel] >= j + 1).mean())
         bj = beta[0, j]
         assert abs(fj - bj) < 4 * math.sqrt(bj * (1 - bj) / sel.sum()), (j, fj, bj)
+
+
+# ------------------------------------------------------------- lenience (l)
+
+def _lenient_law(p, q, l):
+    """Closed form of the emitted token's law for one position under the
+    lenience reading (accept iff u <= min(1, p/(l q)); residual
+    norm(max(0, p - l q))): min(q, p/l) + (1 - sum min(q, p/l)) * r."""
+    acc = np.minimum(q, p / l) if l > 0 else q.copy()
+    res = np.maximum(0.0, p - l * q)
+    r = res / res.sum() if res.sum() > 1e-15 else p
+    return acc + (1.0 - acc.sum()) * r, float(acc.sum())
+
+
+@pytest.mark.parametrize("l", [1.0, 0.5, 0.1])
+def test_lenient_law_single_position(l):
+    """[FI] 'Ablation Studies and Robustness Checks' (Appendix A.5): with a
+    lenience l the acceptance rate is sum min(q, p/l) and, under the stated
+    residual reading, the emitted law is the closed form above; l = 1 is the
+    exact method (law = p).  Exhaustive draft x midpoint-grid enumeration."""
+    rng = np.random.default_rng(61)
+    N = 400
+    for V in (2, 3, 6):
+        zp, q, p = _rand_pq(rng, V, 1)
+        zl, qq, x, u, wts = _grid_batch(zp, q, 1, {}, [0, 1], N)
+        r = oracle.spec_verify_ref(zl, qq, x, u, 1.0, lenience=l)
+        q64 = q[0].astype(np.float64)
+        want, acc = _lenient_law(p[0], q64, l)
+        law = np.bincount(r["out_tokens"][:, 0], weights=wts, minlength=V)
+        assert np.max(np.abs(law - want)) <= 2.0 / N + 1e-6, (l, law, want)
+        assert abs(float(wts[r["n_accepted"] == 1].sum()) - acc) <= 1.0 / N + 1e-6
+        if l == 1.0:
+            assert np.max(np.abs(law - p[0] * q64.sum())) <= 2.0 / N + 1e-6
+
+
+@pytest.mark.parametrize("l", [0.5, 0.2, 0.1])
+def test_lenient_guarantee_p_over_l(l):
+    """[FI] 'How This Work Changes the Landscape': under lenience no token is
+    sampled with probability greater than p(x)/l.  Checked on the oracle's
+    exact law (grid enumeration) for random pairs of rows."""
+    rng = np.random.default_rng(62)
+    N = 300
+    for _ in range(6):
+        V = int(rng.integers(2, 7))
+        zp, q, p = _rand_pq(rng, V, 1)
+        zl, qq, x, u, wts = _grid_batch(zp, q, 1, {}, [0, 1], N)
+        r = oracle.spec_verify_ref(zl, qq, x, u, 1.0, lenience=l)
+        law = np.bincount(r["out_tokens"][:, 0], weights=wts, minlength=V)
+        assert np.all(law <= p[0] / l + 2.0 / N + 1e-6), (law, p[0] / l)
+
+
+def test_lenience_zero_accepts_every_draft_and_one_is_exact():
+    """l = 0 makes p/(l q) infinite: every draft is accepted (the bonus is
+    drawn); l = 1 reproduces the exact method bit for bit."""
+    d = synth.make_inputs("c2", 5, B=6, V=2000)
+    r0 = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                                d["uniforms"], d["temperature"], lenience=0.0)
+    assert np.all(r0["n_accepted"] == d["gamma"])
+    r1 = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                                d["uniforms"], d["temperature"], lenience=1.0)
+    rs = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                                d["uniforms"], d["temperature"])
+    assert np.array_equal(r1["out_tokens"], rs["out_tokens"])
+    with pytest.raises(ValueError):
+        oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
+                               d["uniforms"], d["temperature"], lenience=1.5)
