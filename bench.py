@@ -19,7 +19,8 @@ A second, shorter leg times the same call with the acceptance-rate telemetry
 on (beta for every position, alpha): the row stage then streams every target
 row, and a sweep over target rows 0..gamma-1 and the draft rows (k_beta,
 k_beta_merge) runs before the last launch.  It is reported under
-"telemetry", with the sweep's own roofline.
+"telemetry", with the sweep's own roofline.  A third leg times the lenient
+variant (spec_verify_lenient, l = 0.5) on the same inputs ("lenience").
 """
 from __future__ import annotations
 
@@ -105,6 +106,9 @@ def main():
                     help="minimum wall time of the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--tele-steps", type=int, default=40,
                     help="timed calls with the acceptance-rate telemetry on (0 = skip)")
+    ap.add_argument("--len-steps", type=int, default=40,
+                    help="timed calls of the lenient variant, l = --lenience (0 = skip)")
+    ap.add_argument("--lenience", type=float, default=0.5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -240,6 +244,43 @@ def main():
             "alpha": [round(float(a), 6) for a in alpha.cpu().numpy()],
         }
 
+    lenl = None
+    if args.len_steps > 0:
+        print("[bench] lenience leg", file=sys.stderr, flush=True)
+
+        def lstep(i, events=None):
+            x = dsets[i % 2]
+            sv.spec_verify(x["target_logits"], x["draft_probs"], x["draft_tokens"], x["uniforms"], T,
+                           "sample", n_accepted=n_acc, out_tokens=outs, workspace=ws, events=events,
+                           stream=stream, lenience=args.lenience)
+
+        ln_sets = []
+        for i in range(2):
+            lstep(i)
+            torch.cuda.synchronize()
+            ln_sets.append(n_acc.cpu().numpy().copy())
+        for i in range(4):
+            lstep(i)
+        torch.cuda.synchronize()
+        lev = [(hev.create(), hev.create(), hev.create()) for _ in range(args.len_steps)]
+        t2 = time.perf_counter()
+        for i in range(args.len_steps):
+            lstep(i, events=lev[i])
+        torch.cuda.synchronize()
+        lel = time.perf_counter() - t2
+        l_call = float(np.mean([hev.elapsed_ms(e[0], e[2]) for e in lev]))
+        for e in lev:
+            for h in e:
+                hev.destroy(h)
+        l_bytes = float(np.mean([((n + 1) * V * s_p).sum() + B * gamma * (s_p + s_q)
+                                 + (V * s_p + (n < gamma) * V * s_q).sum() for n in ln_sets]))
+        lenl = {"lenience": args.lenience, "steps": args.len_steps, "ms_per_step": 1e3 * lel / args.len_steps,
+                "seqs_per_s": B * args.len_steps / lel,
+                "tokens_per_s": float(sum((ln_sets[i % 2] + 1).sum() for i in range(args.len_steps))) / lel,
+                "mean_tokens_per_sequence": float(np.mean([(n + 1).mean() for n in ln_sets])),
+                "alg_bytes_per_call": l_bytes,
+                "achieved_GBps": l_bytes / (l_call * 1e-3) / 1e9}
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -273,6 +314,7 @@ def main():
                         "frac": nominal_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "mean_tokens_per_sequence": float(np.mean([(n + 1).mean() for n in n_sets])),
         "telemetry": tele,
+        "lenience": lenl,
     }
     print(json.dumps(line), flush=True)
 

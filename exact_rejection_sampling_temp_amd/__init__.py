@@ -32,7 +32,8 @@ __all__ = [
     "SV_FP32", "SV_BF16", "SV_SAMPLE", "SV_GREEDY", "SV_MAX_GAMMA",
 ]
 
-EXPORTED_SYMBOLS = ("spec_verify", "sv_workspace_bytes", "sv_workspace_init", "sv_status_string")
+EXPORTED_SYMBOLS = ("spec_verify", "spec_verify_lenient", "sv_workspace_bytes", "sv_workspace_init",
+                    "sv_status_string")
 
 
 class SpecVerifyError(RuntimeError):
@@ -88,6 +89,14 @@ def load_library(path: str = LIB_PATH):
             ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+            ctypes.POINTER(Extras), ctypes.c_void_p,
+        ]
+        lib.spec_verify_lenient.restype = ctypes.c_int
+        lib.spec_verify_lenient.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
             ctypes.POINTER(Extras), ctypes.c_void_p,
         ]
@@ -149,7 +158,7 @@ def _dtype_tag(t) -> int:
 
 def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature: float = 1.0,
                 mode: str | int = "sample", *, n_accepted=None, out_tokens=None, workspace=None,
-                aux: dict | None = None, events=None, stream=None):
+                aux: dict | None = None, events=None, stream=None, lenience: float = 1.0):
     """Batched verify-and-sample on the GPU.
 
     target_logits [B, gamma+1, V] fp32/bf16, draft_probs [B, gamma, V] fp32/bf16
@@ -164,6 +173,7 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     makes the call stream every row, see include/spec_verify.h).
     ``events``: optional (begin, mid, end) or (begin, mid, end, tele) raw
     hipEvent_t handles (ints); tele is recorded after the telemetry sweep.
+    ``lenience``: l in [0, 1] (spec_verify_lenient); 1 calls spec_verify.
     """
     import torch
     lib = load_library()
@@ -215,17 +225,20 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
             ex.ev_begin, ex.ev_mid, ex.ev_end = events[:3]
             if len(events) > 3:
                 ex.ev_tele = events[3]
-    rc = lib.spec_verify(
-        B, gamma, V,
-        target_logits.data_ptr(), _dtype_tag(target_logits),
-        draft_probs.data_ptr() if (m == SV_SAMPLE) else None,
-        _dtype_tag(draft_probs) if m == SV_SAMPLE else 0,
-        draft_tokens.data_ptr(), uniforms.data_ptr() if m == SV_SAMPLE else None,
-        float(temperature), m,
-        n_accepted.data_ptr(), out_tokens.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        ctypes.byref(ex) if ex is not None else None,
-        s.cuda_stream)
+    head = (B, gamma, V,
+            target_logits.data_ptr(), _dtype_tag(target_logits),
+            draft_probs.data_ptr() if (m == SV_SAMPLE) else None,
+            _dtype_tag(draft_probs) if m == SV_SAMPLE else 0,
+            draft_tokens.data_ptr(), uniforms.data_ptr() if m == SV_SAMPLE else None,
+            float(temperature))
+    tail = (m, n_accepted.data_ptr(), out_tokens.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            ctypes.byref(ex) if ex is not None else None,
+            s.cuda_stream)
+    if lenience == 1.0:
+        rc = lib.spec_verify(*head, *tail)
+    else:
+        rc = lib.spec_verify_lenient(*head, float(lenience), *tail)
     if rc != SV_OK:
         raise SpecVerifyError(rc)
     return n_accepted, out_tokens

@@ -607,6 +607,7 @@ struct Params {
     uint32_t zero;     // always 0 (see publish)
     float c_hi, c_lo;  // log2(e)/T split into two fp32 terms, c_lo > 0
     double cd;         // log2(e)/T in double
+    double len;        // lenience l in [0, 1] (1: the exact method)
     Exp2Coef ex;       // kExp2Coef
 };
 
@@ -738,7 +739,8 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask)
     if (!(mask & kInvalidBit)) {
         const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
         nMcd = -(double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
-        S_row = __longlong_as_double((long long)ld_agent(sw + 1));
+        // (only decides membership of A = {v : e_v > l q_v S}: scaled by the lenience)
+        S_row = p.len * __longlong_as_double((long long)ld_agent(sw + 1));
     }
     const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
     const void* qrow = static_cast<const char*>(p.probs) +
@@ -778,13 +780,14 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask)
     return false;
 }
 
-// Weight of one element of row n for the inverse-CDF draw: max(0, p - q)
-// with p = e / S, or e itself for the bonus / fallback draw.
+// Weight of one element of row n for the inverse-CDF draw: max(0, p - l q)
+// with p = e / S and l the lenience (1: the exact method), or e itself for
+// the bonus / fallback draw.
 __device__ __forceinline__ double draw_weight(const Params& p, bool use_resid, float z, float q, double nMcd,
                                               double invS)
 {
     const double e = exp2_f64(fma((double)z, p.cd, nMcd), p.ex);
-    return use_resid ? fmax(0.0, e * invS - (double)q) : e;
+    return use_resid ? fmax(0.0, e * invS - p.len * (double)q) : e;
 }
 
 // Clears everything the call left in the workspace for sequence b.  Run by
@@ -882,14 +885,14 @@ __device__ void finish_wave(const Params& p, int b)
             for (int r = 0; r < nrounds; ++r) {
                 if (nrounds > 1) load_round(r);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) zl += fmax(0.0, rEA[i] * invS - rQA[i]);
+                for (int i = 0; i < 8; ++i) zl += fmax(0.0, rEA[i] * invS - p.len * rQA[i]);
             }
         }
         Z = wave_sum(zl);
         const bool use_resid = resid && Z > kResidEps;
         const double total = use_resid ? Z : S;
         const double target = ug * total;
-        auto sub_weight = [&](int i) { return use_resid ? fmax(0.0, rEA[i] * invS - rQA[i]) : rE[i]; };
+        auto sub_weight = [&](int i) { return use_resid ? fmax(0.0, rEA[i] * invS - p.len * rQA[i]) : rE[i]; };
 
         // the sub-chunk whose running weight first exceeds the target: lane
         // totals scanned across the wave, then the crossing lane's entries
@@ -1212,7 +1215,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
             st_agent(slot, (uint64_t)__float_as_uint(mx) | kSlotFlag);
             st_agent(slot + 1, dbits(s) ^ kSignBit);
             if (k < p.gamma && xk >= 0 && xk < p.V) {
-                evidence = rejection_evidence((double)uk, (double)word_elem<PT>(qw, qsel), s, mx,
+                evidence = rejection_evidence((double)uk, p.len * (double)word_elem<PT>(qw, qsel), s, mx,
                                               word_elem<DT>(zw, zsel), p.cd, p.ex);
                 early_bit = 1ull << k;
             }
@@ -1266,13 +1269,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
         uint64_t maskbits = 0;
         if (k < p.gamma) {
             // [FI] Phase 3 / [PB] section 3: accept x_k iff u_k <= min(1, p/q),
-            // q <= 0 accepts ([PB] Reference Implementation).
+            // q <= 0 accepts ([PB] Reference Implementation); with a lenience
+            // l, q is scaled by l first ([FI] Appendix A.5).
             if (xk < 0 || xk >= p.V) {
                 maskbits = kInvalidBit | (1ull << k);
             } else {
                 P = exp2(((double)word_elem<DT>(zw, zsel) - (double)M) * p.cd) / S;
                 Q = (double)word_elem<PT>(qw, qsel);
-                const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / Q);
+                const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / (p.len * Q));
                 if (!((double)uk <= thr)) maskbits = 1ull << k;
             }
         }
@@ -1651,6 +1655,20 @@ int spec_verify(int batch, int gamma, int vocab,
                 void* workspace, size_t workspace_bytes,
                 const sv_extras_t* extras, void* stream)
 {
+    return spec_verify_lenient(batch, gamma, vocab, target_logits, logits_dtype, draft_probs, probs_dtype,
+                               draft_tokens, uniforms, temperature, 1.0f, mode, n_accepted, out_tokens,
+                               workspace, workspace_bytes, extras, stream);
+}
+
+int spec_verify_lenient(int batch, int gamma, int vocab,
+                        const void* target_logits, int logits_dtype,
+                        const void* draft_probs, int probs_dtype,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        float temperature, float lenience, int mode,
+                        int32_t* n_accepted, int32_t* out_tokens,
+                        void* workspace, size_t workspace_bytes,
+                        const sv_extras_t* extras, void* stream)
+{
     // ---- argument validation (no HIP call before this block passes)
     if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_ERR_MODE;
     if (batch < 1) return SV_ERR_BATCH;
@@ -1663,6 +1681,7 @@ int spec_verify(int batch, int gamma, int vocab,
         if (!draft_probs || !uniforms) return SV_ERR_NULL_POINTER;
         if (probs_dtype != SV_FP32 && probs_dtype != SV_BF16) return SV_ERR_DTYPE;
         if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SV_ERR_TEMPERATURE;
+        if (!(lenience >= 0.0f && lenience <= 1.0f)) return SV_ERR_LENIENCE;
     }
     const size_t lsz = logits_dtype == SV_BF16 ? 2 : 4;
     const size_t psz = probs_dtype == SV_BF16 ? 2 : 4;
@@ -1734,6 +1753,7 @@ int spec_verify(int batch, int gamma, int vocab,
     p.c_lo = c_lo;
     p.cd = cd;
     p.ex = kExp2Coef;
+    p.len = greedy ? 1.0 : (double)lenience;
 
     hipEvent_t ev_mid = extras ? (hipEvent_t)extras->ev_mid : nullptr;
     if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)
@@ -1767,6 +1787,7 @@ const char* sv_status_string(int status)
     case SV_ERR_ALIGNMENT: return "a pointer is misaligned for its element type, or the workspace is not 256-byte aligned";
     case SV_ERR_TOO_LARGE: return "problem exceeds the launch-grid limits";
     case SV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case SV_ERR_LENIENCE: return "lenience must be in [0, 1] in sample mode";
     default: return "unknown status";
     }
 }

@@ -67,6 +67,7 @@ extern "C" {
                                    the workspace is not 256-byte aligned             */
 #define SV_ERR_TOO_LARGE -10    /* the problem exceeds the launch-grid limits        */
 #define SV_ERR_LAUNCH -11       /* the HIP runtime rejected a kernel launch          */
+#define SV_ERR_LENIENCE -12     /* sample mode with lenience outside [0, 1]          */
 
 /* Optional outputs for tests and telemetry (every pointer may be NULL;
  * all are device pointers).  Values for positions the walk did not reach
@@ -150,6 +151,31 @@ int spec_verify(int batch, int gamma, int vocab,
                 int32_t* n_accepted, int32_t* out_tokens,
                 void* workspace, size_t workspace_bytes,
                 const sv_extras_t* extras, void* stream);
+
+/*
+ * spec_verify_lenient -- spec_verify with a lenience l in [0, 1] ("Fast
+ * Inference from Transformers via Speculative Decoding", summary page,
+ * "Ablation Studies and Robustness Checks", Appendix A.5: l multiplies
+ * q(x) before it is compared with p(x), for a higher acceptance rate at the
+ * price of exactness; "How This Work Changes the Landscape": no token is
+ * then sampled with probability above p(x)/l).  A draft is accepted iff
+ * u_i <= min(1, p_i(x_i) / (l q_i(x_i))) (q <= 0 accepts); after a rejection
+ * the correction is drawn from norm(max(0, p_n - l q_n)), with the same
+ * fallback to p_n at residual mass <= 1e-15 (the pages give only the
+ * acceptance side; this residual is the same comparison's).  l = 1 is
+ * exactly spec_verify; l = 0 accepts every draft.  resid_mass reports the
+ * lenient residual's mass.  Every other argument as for spec_verify; greedy
+ * mode ignores l.  Returns SV_ERR_LENIENCE for l outside [0, 1] (NaN
+ * included) in sample mode.
+ */
+int spec_verify_lenient(int batch, int gamma, int vocab,
+                        const void* target_logits, int logits_dtype,
+                        const void* draft_probs, int probs_dtype,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        float temperature, float lenience, int mode,
+                        int32_t* n_accepted, int32_t* out_tokens,
+                        void* workspace, size_t workspace_bytes,
+                        const sv_extras_t* extras, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* sv_status_string(int status);

@@ -28,7 +28,8 @@ def to_device(d: dict, device="cuda"):
     return out
 
 
-def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=None, telemetry: bool = False):
+def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=None, telemetry: bool = False,
+            lenience: float = 1.0):
     import torch
     import exact_rejection_sampling_temp_amd as sv
     x = dev_inputs or to_device(d)
@@ -51,7 +52,7 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
         aux["alpha"] = torch.full((G,), float("nan"), dtype=torch.float64, device=dv)
     n, out = sv.spec_verify(x["target_logits"], x.get("draft_probs") if mode == "sample" else None,
                             x["draft_tokens"], x.get("uniforms") if mode == "sample" else None,
-                            d.get("temperature", 1.0), mode, aux=aux)
+                            d.get("temperature", 1.0), mode, aux=aux, lenience=lenience)
     torch.cuda.synchronize()
     # every call must leave the shared workspace all zero (the next call may
     # have another shape, and so another layout of it)
@@ -63,11 +64,12 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
     return res
 
 
-def run_ref(d: dict, mode: str = "sample", telemetry: bool = False):
+def run_ref(d: dict, mode: str = "sample", telemetry: bool = False, lenience: float = 1.0):
     if mode == "greedy":
         return oracle.spec_verify_ref(d["target_logits"], None, d["draft_tokens"], None, 1.0, oracle.GREEDY)
     return oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
-                                  d["uniforms"], d["temperature"], oracle.SAMPLE, telemetry=telemetry)
+                                  d["uniforms"], d["temperature"], oracle.SAMPLE, telemetry=telemetry,
+                                  lenience=lenience)
 
 
 def compare(gpu: dict, ref: dict, gamma: int) -> dict:

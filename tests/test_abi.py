@@ -107,6 +107,23 @@ def test_argument_validation_codes():
     assert _call(mode=sv.SV_GREEDY, probs=None, uniforms=None, T=0.0) == d["SV_ERR_WORKSPACE"]
 
 
+def test_lenient_entry_point_validation():
+    d = _header_defines()
+    lib = sv.load_library()
+
+    def call(l, **kw):
+        a = dict(mode=sv.SV_SAMPLE, T=1.0, ws_bytes=0)
+        a.update(kw)
+        return lib.spec_verify_lenient(2, 3, 100, FAKE, sv.SV_FP32, FAKE, sv.SV_FP32, FAKE, FAKE, a["T"], l,
+                                       a["mode"], FAKE, FAKE, FAKE * 16, a["ws_bytes"], None, None)
+    for bad in (-0.1, 1.01, float("nan"), float("inf")):
+        assert call(bad) == d["SV_ERR_LENIENCE"]
+    for ok in (0.0, 0.5, 1.0):
+        assert call(ok) == d["SV_ERR_WORKSPACE"]  # passes the lenience check, stops at the workspace
+    assert call(2.0, mode=sv.SV_GREEDY) == d["SV_ERR_WORKSPACE"]  # greedy mode ignores l
+    assert call(0.5, T=0.0) == d["SV_ERR_TEMPERATURE"]
+
+
 def test_workspace_init_validation():
     lib = sv.load_library()
     d = _header_defines()
