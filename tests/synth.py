@@ -224,3 +224,27 @@ def make_c1(seed: int, trials: int = 100_000, iid: bool = False) -> dict:
         "rows_zp": zp32, "rows_q": q32,
         "disjoint_rows": np.zeros((trials, gamma), dtype=bool),
     }
+
+
+def make_position_models(L: int, V: int, seed: int, dtype: str = FP32, T: float = 1.0,
+                         sigma: float = 1.0, shift: float = 0.8, iid: bool = False):
+    """Position-only target and draft "models" for the multi-step driver:
+    for each absolute position t, z_q[t] ~ N(0, sigma^2), z_p[t] = z_q[t] +
+    shift * N(0, 1); q[t] = softmax(z_q[t] / T) in fp64 (the draft's output),
+    cast to ``dtype``.  ``iid``: one row pair for every position.  Returns the
+    driver's PositionOnlyModels plus the fp64 target rows for the checks."""
+    from exact_rejection_sampling_temp_amd.driver import PositionOnlyModels
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xF4]))
+    n = 1 if iid else L
+    zq = sigma * rng.standard_normal((n, V))
+    zp = zq + shift * rng.standard_normal((n, V))
+    if iid:
+        zq = np.repeat(zq, L, 0)
+        zp = np.repeat(zp, L, 0)
+    q64 = _softmax64(zq, T)
+    zp_c = _cast(zp, dtype)
+    zp_used = zp_c.astype(np.float64) if dtype == FP32 else bf16_bits_to_f32(zp_c).astype(np.float64)
+    p64 = _softmax64(zp_used, T)
+    m = PositionOnlyModels(target_logits=np.ascontiguousarray(zp_c), draft_probs=_cast(q64, dtype),
+                           draft_probs64=q64, temperature=T)
+    return m, p64
