@@ -20,7 +20,9 @@ on (beta for every position, alpha): the row stage then streams every target
 row, and a sweep over target rows 0..gamma-1 and the draft rows (k_beta,
 k_beta_merge) runs before the last launch.  It is reported under
 "telemetry", with the sweep's own roofline.  A third leg times the lenient
-variant (spec_verify_lenient, l = 0.5) on the same inputs ("lenience").
+variant (spec_verify_lenient, l = 0.5) on the same inputs ("lenience").  A
+last leg runs the multi-step driver ("driver"): 256 streams of 64 tokens over
+c4-shaped position-only models, gamma* from the measured alpha at c = 0.05.
 """
 from __future__ import annotations
 
@@ -109,6 +111,8 @@ def main():
     ap.add_argument("--len-steps", type=int, default=40,
                     help="timed calls of the lenient variant, l = --lenience (0 = skip)")
     ap.add_argument("--lenience", type=float, default=0.5)
+    ap.add_argument("--driver-len", type=int, default=64,
+                    help="tokens per stream of the multi-step driver leg (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -281,6 +285,29 @@ def main():
                 "alg_bytes_per_call": l_bytes,
                 "achieved_GBps": l_bytes / (l_call * 1e-3) / 1e9}
 
+    drv = None
+    if args.driver_len > 0:
+        print("[bench] driver leg", file=sys.stderr, flush=True)
+        from exact_rejection_sampling_temp_amd import driver
+        c_cost = 0.05
+        models, _ = synth.make_position_models(args.driver_len + 64, V, seed=21, dtype=synth.BF16, sigma=3.0,
+                                               shift=1.0)
+        alpha_m = driver.estimate_alpha(models, np.arange(16))
+        g_star = driver.optimal_gamma(alpha_m, c_cost)
+        ver = driver.GpuVerifier(models)
+        driver.speculative_decode(models, B, 8, g_star, seed=1, verify=ver)  # warm-up
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        res = driver.speculative_decode(models, B, args.driver_len, g_star, seed=2, verify=ver)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t3
+        k = np.concatenate(res["accepted"]).astype(float) + 1.0
+        drv = {"streams": int(B), "tokens_per_stream": args.driver_len, "vocab": int(V), "c": c_cost,
+               "alpha_measured": alpha_m, "gamma_star": g_star, "iterations": len(res["accepted"]),
+               "mean_tokens_per_iteration": float(k.mean()),
+               "equation_1_tokens_per_iteration": (1 - alpha_m ** (g_star + 1)) / (1 - alpha_m),
+               "wall_s": dt, "tokens_per_s": B * args.driver_len / dt}
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -315,6 +342,7 @@ def main():
         "mean_tokens_per_sequence": float(np.mean([(n + 1).mean() for n in n_sets])),
         "telemetry": tele,
         "lenience": lenl,
+        "driver": drv,
     }
     print(json.dumps(line), flush=True)
 
