@@ -193,3 +193,30 @@ def argmax_row(z: np.ndarray) -> int:
     lib = _load()
     z = np.ascontiguousarray(z)
     return lib.ref_argmax_row(_ptr(z), _dtype_code(z), z.shape[0])
+
+
+TOPK = 0
+TOPP = 1
+
+
+def standardize(z: np.ndarray, method: int, k: int = 0, top_p: float = 1.0, temperature: float = 1.0):
+    """The oracle's top-k / nucleus standardisation of rows of logits
+    ([R, V] float32 or bf16 bits): returns (logits with dropped entries set
+    to -inf, kept count per row, near-boundary flag per row)."""
+    lib = _load()
+    if not hasattr(lib, "_std_ready"):
+        lib.ref_standardize.restype = ctypes.c_int
+        lib.ref_standardize.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+        lib._std_ready = True
+    z = np.ascontiguousarray(z)
+    R, V = z.shape
+    out = np.empty_like(z)
+    kept = np.empty(R, np.int32)
+    flag = np.empty(R, np.int32)
+    rc = lib.ref_standardize(R, V, _ptr(z), _dtype_code(z), int(method), int(k), float(top_p),
+                             float(temperature), _ptr(out), _ptr(kept), _ptr(flag))
+    if rc != 0:
+        raise ValueError(f"ref_standardize rejected its arguments (status {rc})")
+    return out, kept, flag

@@ -429,3 +429,106 @@ int ref_argmax_row(const void* z, int dtype, int vocab)
     if (vocab < 1 || !z) return -1;
     return argmax_row(z, dtype, 0, vocab);
 }
+
+/* ---- top-k / nucleus standardisation ([FI] "Standardized Sampling") ----
+ *
+ * Top-k: keep the k largest probabilities, zero the rest, renormalise.
+ * Nucleus: sort the probabilities in decreasing order and keep the shortest
+ * prefix whose cumulative probability reaches top_p, zero the rest,
+ * renormalise.  The output is the row of logits with every dropped entry set
+ * to -inf, so that the temperature softmax of the output is exactly the
+ * standardised distribution.  Readings: ties in value are ordered by
+ * increasing index (so top-k keeps exactly min(k, V) entries); the nucleus
+ * prefix includes the entry at which the running sum (fp64, in sorted order,
+ * p_v = exp((z_v - max)/T) / S with S summed in index order) first reaches
+ * top_p; if rounding keeps it below top_p to the end, every entry is kept.
+ * flag (nucleus only): 1 when top_p lies within 1e-9 (relative) of the
+ * running sum just before or at the boundary entry -- a decision that
+ * another summation order may take differently. */
+
+typedef struct {
+    double z;
+    int v;
+} ref_kv_t;
+
+static int kv_desc(const void* a, const void* b)
+{
+    const ref_kv_t* x = (const ref_kv_t*)a;
+    const ref_kv_t* y = (const ref_kv_t*)b;
+    if (x->z > y->z) return -1;
+    if (x->z < y->z) return 1;
+    return x->v < y->v ? -1 : (x->v > y->v ? 1 : 0);
+}
+
+static void store_elem(void* base, int dtype, int64_t idx, const void* src)
+{
+    if (dtype == REF_FP32) ((float*)base)[idx] = ((const float*)src)[idx];
+    else ((uint16_t*)base)[idx] = ((const uint16_t*)src)[idx];
+}
+
+static void store_neg_inf(void* base, int dtype, int64_t idx)
+{
+    if (dtype == REF_FP32) ((float*)base)[idx] = -INFINITY;
+    else ((uint16_t*)base)[idx] = 0xff80u;
+}
+
+#define REF_TOPK 0
+#define REF_TOPP 1
+
+int ref_standardize(int rows, int vocab, const void* z, int dtype, int method, int k, float top_p,
+                    float temperature, void* out, int32_t* kept, int32_t* flag)
+{
+    if (rows < 1 || vocab < 1 || !z || !out) return -1;
+    if (dtype != REF_FP32 && dtype != REF_BF16) return -6;
+    if (method == REF_TOPK && k < 1) return -13;
+    if (method == REF_TOPP && !(top_p > 0.0f && top_p <= 1.0f)) return -13;
+    if (method == REF_TOPP && (!(temperature > 0.0f) || !isfinite(temperature))) return -5;
+    if (method != REF_TOPK && method != REF_TOPP) return -13;
+    int bad = 0;
+#pragma omp parallel
+    {
+        ref_kv_t* kv = (ref_kv_t*)malloc(sizeof(ref_kv_t) * (size_t)vocab);
+        char* keep = (char*)malloc((size_t)vocab);
+        if (!kv || !keep) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < rows; ++r) {
+            if (!kv || !keep) continue;
+            const int64_t off = (int64_t)r * vocab;
+            for (int v = 0; v < vocab; ++v) {
+                kv[v].z = load_elem(z, dtype, off + v);
+                kv[v].v = v;
+            }
+            qsort(kv, (size_t)vocab, sizeof(ref_kv_t), kv_desc);
+            memset(keep, 0, (size_t)vocab);
+            int nk = 0, fl = 0;
+            if (method == REF_TOPK) {
+                nk = k < vocab ? k : vocab;
+            } else {
+                const double m = kv[0].z;
+                double s = 0.0;
+                for (int v = 0; v < vocab; ++v) s += exp((load_elem(z, dtype, off + v) - m) / (double)temperature);
+                double c = 0.0, prev = 0.0;
+                nk = vocab;
+                for (int j = 0; j < vocab; ++j) {
+                    prev = c;
+                    c += exp((kv[j].z - m) / (double)temperature) / s;
+                    if (c >= (double)top_p) { nk = j + 1; break; }
+                }
+                if (near_boundary((double)top_p, prev, 1e-9) || near_boundary((double)top_p, c, 1e-9)) fl = 1;
+            }
+            for (int j = 0; j < nk; ++j) keep[kv[j].v] = 1;
+            for (int v = 0; v < vocab; ++v) {
+                if (keep[v]) store_elem(out, dtype, off + v, z);
+                else store_neg_inf(out, dtype, off + v);
+            }
+            if (kept) kept[r] = nk;
+            if (flag) flag[r] = fl;
+        }
+        free(kv);
+        free(keep);
+    }
+    return bad ? -10 : 0;
+}

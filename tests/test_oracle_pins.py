@@ -634,3 +634,101 @@ def test_lenience_zero_accepts_every_draft_and_one_is_exact():
     with pytest.raises(ValueError):
         oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
                                d["uniforms"], d["temperature"], lenience=1.5)
+
+
+# ------------------------------------- top-k / nucleus standardisation (f2)
+
+def _rows_with_ties(rng, R, V, dtype):
+    z = np.round(rng.standard_normal((R, V)) * 2, 1).astype(np.float32)   # many exact ties
+    z[:, rng.integers(0, V, 3)] = -np.inf
+    if dtype == "bf16":
+        zb = synth.f32_to_bf16_bits(z)
+        return zb, synth.bf16_bits_to_f32(zb)
+    return z, z
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_topk_matches_a_stable_sort(dtype):
+    """[FI] 'Standardized Sampling', top-k: the k largest entries survive.
+    Reference: numpy's stable argsort of -z (ties in index order), first k."""
+    rng = np.random.default_rng(71)
+    V = 300
+    z, zf = _rows_with_ties(rng, 12, V, dtype)
+    for k in (1, 2, 7, 50, V - 1, V, V + 5):
+        out, kept, _ = oracle.standardize(z, oracle.TOPK, k=k)
+        outf = out if dtype == "fp32" else synth.bf16_bits_to_f32(out)
+        for r in range(z.shape[0]):
+            keep = np.zeros(V, bool)
+            keep[np.argsort(-zf[r], kind="stable")[:min(k, V)]] = True
+            want = np.where(keep, zf[r], -np.inf)
+            assert np.array_equal(outf[r], want), (k, r)
+            assert kept[r] == min(k, V)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_topp_matches_a_sorted_running_sum(dtype):
+    """[FI] 'Standardized Sampling', nucleus: sort the probabilities, keep the
+    shortest prefix whose running sum reaches top_p.  Reference: scipy's
+    softmax, numpy's stable argsort and cumsum; rows the oracle flags as
+    within 1e-9 of the boundary are skipped (other summation orders)."""
+    rng = np.random.default_rng(72)
+    V = 400
+    z, zf = _rows_with_ties(rng, 16, V, dtype)
+    checked = 0
+    for T in (0.7, 1.0):
+        for top_p in (0.05, 0.3, 0.9, 0.999, 1.0):
+            out, kept, flag = oracle.standardize(z, oracle.TOPP, top_p=top_p, temperature=T)
+            outf = out if dtype == "fp32" else synth.bf16_bits_to_f32(out)
+            for r in range(z.shape[0]):
+                if flag[r]:
+                    continue
+                # (the temperature reaches the oracle as fp32)
+                p = scipy.special.softmax(zf[r].astype(np.float64) / float(np.float32(T)))
+                order = np.argsort(-zf[r], kind="stable")
+                c = np.cumsum(p[order])
+                hit = np.nonzero(c >= float(np.float32(top_p)))[0]  # top_p also arrives as fp32
+                nk = int(hit[0]) + 1 if hit.size else V
+                keep = np.zeros(V, bool)
+                keep[order[:nk]] = True
+                assert np.array_equal(outf[r], np.where(keep, zf[r], -np.inf)), (T, top_p, r)
+                assert kept[r] == nk
+                checked += 1
+    assert checked > 100
+
+
+def test_topk_one_is_the_argmax_and_full_k_is_identity():
+    """k = 1 leaves the point mass at the first maximum ([FI]'s argmax case);
+    k = V (and top_p below the largest probability / top_p = 1) as stated."""
+    rng = np.random.default_rng(73)
+    z, _ = _rows_with_ties(rng, 8, 64, "fp32")
+    out, _, _ = oracle.standardize(z, oracle.TOPK, k=1)
+    for r in range(8):
+        assert np.nonzero(np.isfinite(out[r]))[0].tolist() == [oracle.argmax_row(z[r])]
+    out, _, _ = oracle.standardize(z, oracle.TOPK, k=64)
+    assert np.array_equal(out, z)
+    out, kept, _ = oracle.standardize(z, oracle.TOPP, top_p=1e-6)
+    assert np.all(kept == 1)
+    out, kept, _ = oracle.standardize(z, oracle.TOPP, top_p=1.0)
+    assert np.all(kept >= np.isfinite(z).sum(1) - 1)
+
+
+def test_standardised_verification_is_exact():
+    """[FI] 'Standardized Sampling': with p and q both standardised (top-k
+    here), the verify step emits the standardised p exactly.  Exhaustive
+    draft x midpoint-grid enumeration on tiny rows."""
+    rng = np.random.default_rng(74)
+    N = 300
+    for V, k in ((5, 3), (6, 2)):
+        zq = rng.standard_normal(V)
+        zp = (zq + 0.8 * rng.standard_normal(V)).astype(np.float32)
+        zp_std, _, _ = oracle.standardize(np.stack([zp, zp]), oracle.TOPK, k=k)
+        q = scipy.special.softmax(zq)
+        q[np.argsort(-q, kind="stable")[k:]] = 0.0
+        q = (q / q.sum()).astype(np.float32)
+        zl, qq, x, u, wts = _grid_batch(zp_std, q[None, :], 1, {}, [0, 1], N)
+        r = oracle.spec_verify_ref(zl, qq, x, u, 1.0)
+        law = np.bincount(r["out_tokens"][:, 0], weights=wts, minlength=V)
+        p = scipy.special.softmax(zp.astype(np.float64))
+        p[np.argsort(-zp, kind="stable")[k:]] = 0.0
+        p /= p.sum()
+        assert np.max(np.abs(law - p * float(q.astype(np.float64).sum()))) <= 2.0 / N + 1e-6
