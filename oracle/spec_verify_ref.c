@@ -441,7 +441,9 @@ int ref_argmax_row(const void* z, int dtype, int vocab)
  * increasing index (so top-k keeps exactly min(k, V) entries); the nucleus
  * prefix includes the entry at which the running sum (fp64, in sorted order,
  * p_v = exp((z_v - max)/T) / S with S summed in index order) first reaches
- * top_p; if rounding keeps it below top_p to the end, every entry is kept.
+ * top_p; if rounding keeps it below top_p to the end, every entry is kept,
+ * and top_p = 1 keeps every entry (the whole distribution: only rounding
+ * could make a running sum reach 1 before the last positive entry).
  * flag (nucleus only): 1 when top_p lies within 1e-9 (relative) of the
  * running sum just before or at the boundary entry -- a decision that
  * another summation order may take differently. */
@@ -506,6 +508,8 @@ int ref_standardize(int rows, int vocab, const void* z, int dtype, int method, i
             int nk = 0, fl = 0;
             if (method == REF_TOPK) {
                 nk = k < vocab ? k : vocab;
+            } else if (top_p >= 1.0f) {
+                nk = vocab;
             } else {
                 const double m = kv[0].z;
                 double s = 0.0;
