@@ -25,15 +25,17 @@ SV_SAMPLE = 0
 SV_GREEDY = 1
 SV_MAX_GAMMA = 62
 SV_OK = 0
+SV_TOPK = 0
+SV_TOPP = 1
 
 __all__ = [
-    "spec_verify", "sv_workspace_bytes", "sv_workspace_init", "sv_status_string",
+    "spec_verify", "standardize", "sv_workspace_bytes", "sv_workspace_init", "sv_status_string",
     "SpecVerifyError", "load_library", "EXPORTED_SYMBOLS",
     "SV_FP32", "SV_BF16", "SV_SAMPLE", "SV_GREEDY", "SV_MAX_GAMMA",
 ]
 
 EXPORTED_SYMBOLS = ("spec_verify", "spec_verify_lenient", "sv_workspace_bytes", "sv_workspace_init",
-                    "sv_status_string")
+                    "sv_status_string", "sv_standardize")
 
 
 class SpecVerifyError(RuntimeError):
@@ -92,6 +94,10 @@ def load_library(path: str = LIB_PATH):
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
             ctypes.POINTER(Extras), ctypes.c_void_p,
         ]
+        lib.sv_standardize.restype = ctypes.c_int
+        lib.sv_standardize.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                       ctypes.c_void_p]
         lib.spec_verify_lenient.restype = ctypes.c_int
         lib.spec_verify_lenient.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -242,3 +248,32 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     if rc != SV_OK:
         raise SpecVerifyError(rc)
     return n_accepted, out_tokens
+
+
+def standardize(logits, method: str | int, k: int = 0, top_p: float = 1.0, temperature: float = 1.0, *,
+                out=None, stream=None):
+    """Top-k ("topk", k) or nucleus ("topp", top_p at temperature T)
+    standardisation of the rows of ``logits`` (any shape [..., V], fp32 or
+    bf16, contiguous, on the GPU): returns ``out`` (new, or the given tensor,
+    which may be ``logits`` itself) holding the rows with every dropped entry
+    set to -inf (sv_standardize in include/spec_verify.h)."""
+    import torch
+    lib = load_library()
+    m = method if isinstance(method, int) else {"topk": SV_TOPK, "topp": SV_TOPP}[method]
+    if logits.device.type != "cuda":
+        raise ValueError("standardize runs on the GPU only")
+    if not logits.is_contiguous() or logits.dim() < 1:
+        raise ValueError("logits must be a contiguous tensor [..., V]")
+    V = logits.shape[-1]
+    rows = logits.numel() // max(V, 1)
+    if out is None:
+        out = torch.empty_like(logits)
+    elif out.shape != logits.shape or out.dtype != logits.dtype or out.device != logits.device or \
+            not out.is_contiguous():
+        raise ValueError("out must match logits")
+    s = stream if stream is not None else torch.cuda.current_stream(logits.device)
+    rc = lib.sv_standardize(rows, V, logits.data_ptr(), _dtype_tag(logits), m, int(k), float(top_p),
+                            float(temperature), out.data_ptr(), s.cuda_stream)
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "sv_standardize")
+    return out

@@ -1,13 +1,14 @@
-"""Build step of the HIP library: compiles csrc/*.hip for gfx950 into an
+"""Build step of the HIP library: compiles csrc/*.hip for gfx950 into one
 in-tree shared library, libspecverify.so, next to this file."""
 from __future__ import annotations
 
+import glob
 import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "spec_verify.hip")
+SRCS = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
 ARCH = "gfx950"
@@ -24,7 +25,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SRCS]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("HIP build failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)

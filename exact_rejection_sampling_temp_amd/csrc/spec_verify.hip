@@ -1788,6 +1788,7 @@ const char* sv_status_string(int status)
     case SV_ERR_TOO_LARGE: return "problem exceeds the launch-grid limits";
     case SV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SV_ERR_LENIENCE: return "lenience must be in [0, 1] in sample mode";
+    case SV_ERR_STANDARDIZE: return "standardisation needs SV_TOPK with k >= 1 or SV_TOPP with 0 < top_p <= 1";
     default: return "unknown status";
     }
 }

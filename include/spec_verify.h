@@ -68,6 +68,11 @@ extern "C" {
 #define SV_ERR_TOO_LARGE -10    /* the problem exceeds the launch-grid limits        */
 #define SV_ERR_LAUNCH -11       /* the HIP runtime rejected a kernel launch          */
 #define SV_ERR_LENIENCE -12     /* sample mode with lenience outside [0, 1]          */
+#define SV_ERR_STANDARDIZE -13  /* unknown method, k < 1, or top_p outside (0, 1]    */
+
+/* Standardisation methods (sv_standardize). */
+#define SV_TOPK 0
+#define SV_TOPP 1
 
 /* Optional outputs for tests and telemetry (every pointer may be NULL;
  * all are device pointers).  Values for positions the walk did not reach
@@ -176,6 +181,37 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
                         int32_t* n_accepted, int32_t* out_tokens,
                         void* workspace, size_t workspace_bytes,
                         const sv_extras_t* extras, void* stream);
+
+/*
+ * sv_standardize -- top-k or nucleus (top-p) standardisation of rows of
+ * target logits ("Fast Inference from Transformers via Speculative
+ * Decoding", summary page, "Standardized Sampling": top-k keeps the k
+ * largest probabilities, nucleus sorts them and keeps those up to the point
+ * where the running sum reaches top_p, and both renormalise; the verify step
+ * then compares these standardised distributions).  For each of `rows` rows
+ * of `vocab` logits, writes the row to logits_out with every dropped entry
+ * set to -inf, so that softmax(out / T) is exactly the standardised
+ * distribution and spec_verify can take logits_out as its target_logits.
+ *
+ *   rows, vocab    R >= 1 rows of V >= 1 entries, contiguous, row-major
+ *   logits         [R][V] device, dtype SV_FP32 or SV_BF16; finite or -inf
+ *   method         SV_TOPK (k >= 1; k >= V keeps the row) or SV_TOPP
+ *                  (0 < top_p <= 1, temperature T > 0 finite: the nucleus is
+ *                  taken on softmax(z / T))
+ *   logits_out     [R][V] device, same dtype; may equal logits (in place)
+ *   stream         hipStream_t
+ *
+ * Ties in value are ordered by index: top-k keeps exactly min(k, V)
+ * entries, and the nucleus keeps the shortest prefix of the order (value
+ * decreasing, index increasing) whose probability reaches top_p (every
+ * entry if rounding keeps the running sum below top_p; top_p = 1 keeps
+ * every entry).  -0 and +0 are
+ * equal values.  The draft side standardises its own q before sampling
+ * (the caller's q is used as given).  Returns SV_OK after enqueueing, or
+ * SV_ERR_* without touching any buffer.
+ */
+int sv_standardize(int rows, int vocab, const void* logits, int dtype, int method, int k, float top_p,
+                   float temperature, void* logits_out, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* sv_status_string(int status);

@@ -248,3 +248,28 @@ def make_position_models(L: int, V: int, seed: int, dtype: str = FP32, T: float 
     m = PositionOnlyModels(target_logits=np.ascontiguousarray(zp_c), draft_probs=_cast(q64, dtype),
                            draft_probs64=q64, temperature=T)
     return m, p64
+
+
+def standardize_draft_topk(d: dict, k: int, seed: int) -> dict:
+    """The draft model's own top-k standardisation (its part of "Standardized
+    Sampling"): each draft row keeps its k largest probabilities (ties in
+    index order), renormalised in fp64 and cast back; the draft tokens are
+    redrawn from the standardised rows.  Returns a new input dict."""
+    out = dict(d)
+    q = d["draft_probs"]
+    q64 = (q.astype(np.float64) if q.dtype == np.float32 else bf16_bits_to_f32(q).astype(np.float64))
+    B, G, V = q64.shape
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xF2]))
+    qs = np.zeros_like(q64)
+    x = np.empty((B, G), np.int32)
+    for b in range(B):
+        for i in range(G):
+            keep = np.argsort(-q64[b, i], kind="stable")[:k]
+            row = np.zeros(V)
+            row[keep] = q64[b, i, keep]
+            row /= row.sum()
+            qs[b, i] = row
+        x[b] = _sample_rows(rng, qs[b])
+    out["draft_probs"] = _cast(qs, FP32 if q.dtype == np.float32 else BF16)
+    out["draft_tokens"] = x
+    return out

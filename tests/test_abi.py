@@ -124,6 +124,26 @@ def test_lenient_entry_point_validation():
     assert call(0.5, T=0.0) == d["SV_ERR_TEMPERATURE"]
 
 
+def test_standardize_validation():
+    d = _header_defines()
+    lib = sv.load_library()
+
+    def call(rows=2, V=100, z=FAKE, dt=sv.SV_FP32, m=sv.SV_TOPK, k=5, p=0.9, T=1.0, out=FAKE):
+        return lib.sv_standardize(rows, V, z, dt, m, k, p, T, out, None)
+    assert call(z=None) == d["SV_ERR_NULL_POINTER"]
+    assert call(out=None) == d["SV_ERR_NULL_POINTER"]
+    assert call(rows=0) == d["SV_ERR_BATCH"]
+    assert call(V=0) == d["SV_ERR_VOCAB"]
+    assert call(dt=7) == d["SV_ERR_DTYPE"]
+    assert call(m=5) == d["SV_ERR_STANDARDIZE"]
+    assert call(k=0) == d["SV_ERR_STANDARDIZE"]
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        assert call(m=sv.SV_TOPP, p=bad) == d["SV_ERR_STANDARDIZE"]
+    assert call(m=sv.SV_TOPP, T=0.0) == d["SV_ERR_TEMPERATURE"]
+    assert call(z=FAKE + 2) == d["SV_ERR_ALIGNMENT"]
+    assert d["SV_TOPK"] == sv.SV_TOPK and d["SV_TOPP"] == sv.SV_TOPP
+
+
 def test_workspace_init_validation():
     lib = sv.load_library()
     d = _header_defines()
