@@ -23,6 +23,8 @@ k_beta_merge) runs before the last launch.  It is reported under
 variant (spec_verify_lenient, l = 0.5) on the same inputs ("lenience").  A
 last leg runs the multi-step driver ("driver"): 256 streams of 64 tokens over
 c4-shaped position-only models, gamma* from the measured alpha at c = 0.05.
+"standardize" times sv_standardize (top-k k = 50, nucleus top_p = 0.9) over
+the 2 304 target rows of the c4 batch.
 """
 from __future__ import annotations
 
@@ -113,6 +115,8 @@ def main():
     ap.add_argument("--lenience", type=float, default=0.5)
     ap.add_argument("--driver-len", type=int, default=64,
                     help="tokens per stream of the multi-step driver leg (0 = skip)")
+    ap.add_argument("--std-steps", type=int, default=20,
+                    help="timed calls of each standardisation (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -308,6 +312,30 @@ def main():
                "equation_1_tokens_per_iteration": (1 - alpha_m ** (g_star + 1)) / (1 - alpha_m),
                "wall_s": dt, "tokens_per_s": B * args.driver_len / dt}
 
+    stdz = None
+    if args.std_steps > 0:
+        print("[bench] standardize leg", file=sys.stderr, flush=True)
+        zrows = dsets[0]["target_logits"].reshape(-1, V)
+        zout = torch.empty_like(zrows)
+        stdz = {"rows": int(zrows.shape[0]), "vocab": int(V), "dtype": "bf16"}
+        rows_bytes = 2.0 * zrows.numel() * 2  # one read and one write of every row
+        for name, kw in (("topk_k50", dict(method="topk", k=50)), ("topp_0.9", dict(method="topp", top_p=0.9))):
+            for _ in range(3):
+                sv.standardize(zrows, out=zout, stream=stream, **kw)
+            torch.cuda.synchronize()
+            e0, e1 = hev.create(), hev.create()
+            hev.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hev.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
+            for _ in range(args.std_steps):
+                sv.standardize(zrows, out=zout, stream=stream, **kw)
+            hev.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
+            torch.cuda.synchronize()
+            ms = hev.elapsed_ms(e0, e1) / args.std_steps
+            hev.destroy(e0)
+            hev.destroy(e1)
+            stdz[name] = {"ms_per_call": ms, "alg_bytes": rows_bytes,
+                          "achieved_GBps": rows_bytes / (ms * 1e-3) / 1e9}
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -343,6 +371,7 @@ def main():
         "telemetry": tele,
         "lenience": lenl,
         "driver": drv,
+        "standardize": stdz,
     }
     print(json.dumps(line), flush=True)
 

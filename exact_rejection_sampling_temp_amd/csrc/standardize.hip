@@ -10,7 +10,8 @@
 // entry set to -inf, so the temperature softmax of the output is exactly the
 // renormalised kept set, and spec_verify runs on it unchanged.
 //
-// One 1024-thread workgroup per row.  The kept set is found by an MSB-first
+// One workgroup per row (512 threads for top-k, two rows per CU; 1024 for
+// the nucleus).  The kept set is found by an MSB-first
 // radix select over order-preserving integer keys of the logits (12-bit then
 // 4-bit digits for bf16; 12, 12, 8 for fp32): a pass over the row builds the
 // digit's histogram in LDS (element counts, and for nucleus the fp64 masses
@@ -30,10 +31,17 @@
 
 namespace {
 
-constexpr int kSThreads = 1024;
-constexpr int kSWaves = kSThreads / 64;
+// workgroup size: 512 threads for top-k (two rows per CU), 1024 for the
+// nucleus, whose fp64 mass atomics and polynomial need the registers
+template <bool NUCLEUS>
+struct StdShape {
+    static constexpr int kSThreads = NUCLEUS ? 1024 : 512;
+    static constexpr int kSWaves = kSThreads / 64;
+    static constexpr int kBinsPerThread = 4096 / kSThreads;
+};
+constexpr int kMaxWaves = 16;
 constexpr int kBins = 4096;  // 12-bit digits
-constexpr int kBinsPerThread = kBins / kSThreads;
+constexpr int kUnroll = 4;  // groups of 8 entries per thread per histogram iteration
 
 struct StdParams {
     const void* in;
@@ -105,6 +113,27 @@ __device__ __forceinline__ void load8(const void* row, int base, int V, uint32_t
     }
 }
 
+// 2^a in fp64: round to the nearest integer n, a degree-9 polynomial for
+// 2^f on f in [-1/2, 1/2] (Taylor coefficients (ln 2)^i / i! of e^(f ln 2);
+// relative error below 7e-12, far inside the 1e-9 window the nucleus
+// boundary is judged in), then ldexp.  a <= 0 here (entries relative to the
+// row maximum).
+__device__ __forceinline__ double exp2_fast(double a)
+{
+    constexpr double kMagic = 6755399441055744.0;  // 1.5 * 2^52
+    a = fmax(a, -1100.0);
+    const double t = a + kMagic;
+    const double f = a - (t - kMagic);
+    const int n = __double2loint(t);
+    constexpr double c[10] = {1.0, 0.6931471805599453, 0.2402265069591007, 0.05550410866482158,
+                              0.009618129107628477, 0.0013333558146428443, 0.00015403530393381606,
+                              1.525273380405984e-05, 1.3215486790144307e-06, 1.0178086009239699e-07};
+    double p = c[9];
+#pragma unroll
+    for (int i = 8; i >= 0; --i) p = fma(f, p, c[i]);
+    return ldexp(p, n);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan_t(T v)
 {
@@ -122,12 +151,14 @@ template <typename T>
 __device__ T block_excl_scan(T v, T* sm, T* total)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int kSWaves = (int)(blockDim.x >> 6);
     const T incl = wave_incl_scan_t(v);
     if (lane == 63) sm[w] = incl;
     __syncthreads();
     T before = T(0), all = T(0);
 #pragma unroll
-    for (int i = 0; i < kSWaves; ++i) {
+    for (int i = 0; i < kMaxWaves; ++i) {
+        if (i >= kSWaves) break;
         const T s = sm[i];
         if (i < w) before += s;
         all += s;
@@ -144,20 +175,21 @@ __device__ uint32_t block_max_u32(uint32_t v, uint32_t* sm)
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
     __syncthreads();
     uint32_t r = 0;
-#pragma unroll
-    for (int i = 0; i < kSWaves; ++i) r = max(r, sm[i]);
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = max(r, sm[i]);
     __syncthreads();
     return r;
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kSThreads) void k_standardize(const StdParams sp)
+template <int DT, bool VEC, bool NUCLEUS>
+__global__ __launch_bounds__(StdShape<NUCLEUS>::kSThreads) void k_standardize(const StdParams sp)
 {
+    constexpr int kSThreads = StdShape<NUCLEUS>::kSThreads;
+    constexpr int kBinsPerThread = StdShape<NUCLEUS>::kBinsPerThread;
     constexpr int KB = DT == SV_BF16 ? 16 : 32;
     constexpr int NPASS = DT == SV_BF16 ? 2 : 3;
     constexpr int kShift[3] = {KB - 12, DT == SV_BF16 ? 0 : 8, 0};
     constexpr int kDigit[3] = {12, DT == SV_BF16 ? 4 : 12, 8};
-    const bool nucleus = sp.method == SV_TOPP;
+    constexpr bool nucleus = NUCLEUS;
     const int tid = (int)threadIdx.x;
     const int V = sp.V;
     const size_t es = DT == SV_BF16 ? 2 : 4;
@@ -167,8 +199,8 @@ __global__ __launch_bounds__(kSThreads) void k_standardize(const StdParams sp)
 
     __shared__ uint32_t h_cnt[kBins];
     __shared__ double h_mass[kBins];
-    __shared__ uint32_t sm_u[kSWaves];
-    __shared__ double sm_d[kSWaves];
+    __shared__ uint32_t sm_u[kMaxWaves];
+    __shared__ double sm_d[kMaxWaves];
     __shared__ uint32_t sm_bin;
     __shared__ uint32_t sm_above_cnt;
     __shared__ double sm_above_mass;
@@ -201,12 +233,24 @@ __global__ __launch_bounds__(kSThreads) void k_standardize(const StdParams sp)
             h_mass[i] = 0.0;
         }
         __syncthreads();
-        for (int g = tid; g < ngroups; g += kSThreads) {
-            uint32_t bits[8];
-            bool ok[8];
-            load8<DT, VEC>(row, g * 8, V, bits, ok);
+        for (int g0 = tid; g0 < ngroups; g0 += kUnroll * kSThreads) {
+            uint32_t bitsu[kUnroll][8];
+            bool oku[kUnroll][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int u = 0; u < kUnroll; ++u) {  // every load of the iteration in flight at once
+                const int g = g0 + u * kSThreads;
+                if (g < ngroups) {
+                    load8<DT, VEC>(row, g * 8, V, bitsu[u], oku[u]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) { bitsu[u][e] = 0u; oku[u][e] = false; }
+                }
+            }
+#pragma unroll
+            for (int ue = 0; ue < kUnroll * 8; ++ue) {
+                const int e = ue & 7;
+                const uint32_t (&bits)[8] = bitsu[ue >> 3];
+                const bool (&ok)[8] = oku[ue >> 3];
                 const uint32_t key = key_of<DT>(bits[e]);
                 const uint32_t hi = shift + dbits >= 32 ? 0u : (key >> (shift + dbits));
                 if (!ok[e] || hi != prefix) continue;
@@ -214,7 +258,7 @@ __global__ __launch_bounds__(kSThreads) void k_standardize(const StdParams sp)
                 atomicAdd(&h_cnt[bin], 1u);
                 if (nucleus) {
                     const float z = value_of_bits<DT>(bits[e]);
-                    if (z > -INFINITY) atomicAdd(&h_mass[bin], exp2(((double)z - m) * sp.cd));
+                    if (z > -INFINITY) atomicAdd(&h_mass[bin], exp2_fast(((double)z - m) * sp.cd));
                 }
             }
         }
@@ -266,7 +310,7 @@ __global__ __launch_bounds__(kSThreads) void k_standardize(const StdParams sp)
     const uint32_t kstar = prefix;
     uint32_t need = rem_cnt;
     if (!keep_all && nucleus) {
-        const double wt = exp2(((double)value_of_key<DT>(kstar) - m) * sp.cd);
+        const double wt = exp2_fast(((double)value_of_key<DT>(kstar) - m) * sp.cd);
         const double n = ceil(rem_mass / wt);
         need = n < 1.0 ? 1u : (n > 4294967295.0 ? 0xffffffffu : (uint32_t)n);
     }
@@ -337,12 +381,24 @@ extern "C" int sv_standardize(int rows, int vocab, const void* logits, int dtype
     sp.cd = method == SV_TOPP ? 1.4426950408889634 / (double)temperature : 0.0;
     const bool vec = aligned_to(logits, 16) && ((size_t)vocab * es) % 16 == 0;
     hipStream_t s = (hipStream_t)stream;
+    const bool nuc = method == SV_TOPP;
+    const dim3 g(rows), t(nuc ? StdShape<true>::kSThreads : StdShape<false>::kSThreads);
     if (dtype == SV_BF16) {
-        if (vec) hipLaunchKernelGGL((k_standardize<SV_BF16, true>), dim3(rows), dim3(kSThreads), 0, s, sp);
-        else hipLaunchKernelGGL((k_standardize<SV_BF16, false>), dim3(rows), dim3(kSThreads), 0, s, sp);
+        if (vec) {
+            if (nuc) hipLaunchKernelGGL((k_standardize<SV_BF16, true, true>), g, t, 0, s, sp);
+            else hipLaunchKernelGGL((k_standardize<SV_BF16, true, false>), g, t, 0, s, sp);
+        } else {
+            if (nuc) hipLaunchKernelGGL((k_standardize<SV_BF16, false, true>), g, t, 0, s, sp);
+            else hipLaunchKernelGGL((k_standardize<SV_BF16, false, false>), g, t, 0, s, sp);
+        }
     } else {
-        if (vec) hipLaunchKernelGGL((k_standardize<SV_FP32, true>), dim3(rows), dim3(kSThreads), 0, s, sp);
-        else hipLaunchKernelGGL((k_standardize<SV_FP32, false>), dim3(rows), dim3(kSThreads), 0, s, sp);
+        if (vec) {
+            if (nuc) hipLaunchKernelGGL((k_standardize<SV_FP32, true, true>), g, t, 0, s, sp);
+            else hipLaunchKernelGGL((k_standardize<SV_FP32, true, false>), g, t, 0, s, sp);
+        } else {
+            if (nuc) hipLaunchKernelGGL((k_standardize<SV_FP32, false, true>), g, t, 0, s, sp);
+            else hipLaunchKernelGGL((k_standardize<SV_FP32, false, false>), g, t, 0, s, sp);
+        }
     }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
