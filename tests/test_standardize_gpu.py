@@ -113,3 +113,41 @@ def test_verify_on_standardised_rows(k):
         n = r["n_accepted"][b]
         t = g["out_tokens"][b, n]
         assert zs[b, n, t] != 0xff80
+
+
+@pytest.mark.parametrize("method,kw", [("topk", dict(k=9)), ("topk", dict(k=999)), ("topp", dict(top_p=0.6)),
+                                       ("topp", dict(top_p=0.95, T=0.8))])
+def test_bf16_rows_with_ties_inf_and_signed_zero(method, kw):
+    """bf16 rows rounded to few distinct values (long runs of ties), -inf
+    entries and both zeros: the 16-bit key histogram, the tie counts per
+    wave run and the packed output pass."""
+    rng = np.random.default_rng(11)
+    z = np.round(rng.standard_normal((16, 50_000)) * 2, 1).astype(np.float32)
+    z[:, rng.integers(0, 50_000, 300)] = -np.inf
+    z[:, 100:140] = 0.0
+    z[:, 140:180] = -0.0
+    _check(synth.f32_to_bf16_bits(z), method, **kw)
+
+
+@pytest.mark.parametrize("method,kw", [("topk", dict(k=5)), ("topk", dict(k=66_500)), ("topp", dict(top_p=0.5)),
+                                       ("topp", dict(top_p=0.999))])
+def test_bf16_value_repeated_past_16_bit_counts(method, kw):
+    """One value occurs 66 000 times in a row of 70 000: its 16-bit counter
+    wraps, the total count shows it, and the row takes the radix select."""
+    rng = np.random.default_rng(12)
+    V = 70_000
+    z = (rng.standard_normal((4, V)) * 2).astype(np.float32)
+    for r in range(4):
+        z[r, rng.permutation(V)[:66_000]] = 0.5 if r % 2 == 0 else -1.25
+    _check(synth.f32_to_bf16_bits(z), method, **kw)
+
+
+@pytest.mark.parametrize("method,kw", [("topk", dict(k=30_000)), ("topk", dict(k=3)), ("topp", dict(top_p=0.5)),
+                                       ("topp", dict(top_p=0.97, T=2.0))])
+def test_bf16_long_tie_runs(method, kw):
+    """bf16 rows of ~7 distinct values over 150 000 entries: the final key
+    has tens of thousands of ties, more than a wave's tie list holds, so the
+    wave holding the last kept tie ranks its run again."""
+    rng = np.random.default_rng(13)
+    z = np.round(rng.standard_normal((6, 150_000))).astype(np.float32)
+    _check(synth.f32_to_bf16_bits(z), method, **kw)
