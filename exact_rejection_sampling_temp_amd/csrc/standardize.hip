@@ -40,8 +40,8 @@
 // its own: a wave whose run lies wholly before the last kept tie or wholly
 // after it keeps entries by a key threshold (for bf16 two entries per 32-bit
 // operation), and only a wave whose run holds the last kept tie ranks its
-// ties in index order.  The output is written with 128-bit stores where the
-// row allows.
+// ties in index order.  The output is written with 128-bit nontemporal
+// stores where the row allows.
 
 #include <hip/hip_runtime.h>
 
@@ -186,6 +186,15 @@ __device__ __forceinline__ uint32_t bits_of(const G8& g, int e)
     }
 }
 __device__ __forceinline__ uint32_t word_of(const uint4& a, int i) { return i == 0 ? a.x : i == 1 ? a.y : i == 2 ? a.z : a.w; }
+
+// 16-byte store of the output, nontemporal: the output is not read again
+// here, and streaming it past the caches leaves them to the input rows
+// (measured 1-3 % faster on the c4 rows)
+__device__ __forceinline__ void store16(void* p, uint4 v)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
 
 // 2^a in fp64: round to the nearest integer n, a degree-9 polynomial for
 // 2^f on f in [-1/2, 1/2] (Taylor coefficients (ln 2)^i / i! of e^(f ln 2);
@@ -497,9 +506,9 @@ __device__ __forceinline__ uint32_t write_row(const StdParams& sp, const void* r
                 uint32_t k2[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) k2[i] = keys2(word_of(a, i));
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(orow) + g * 8) =
-                    make_uint4(keep2(a.x, k2[0], kc2), keep2(a.y, k2[1], kc2), keep2(a.z, k2[2], kc2),
-                               keep2(a.w, k2[3], kc2));
+                store16(static_cast<uint16_t*>(orow) + g * 8,
+                        make_uint4(keep2(a.x, k2[0], kc2), keep2(a.y, k2[1], kc2), keep2(a.z, k2[2], kc2),
+                                   keep2(a.w, k2[3], kc2)));
                 if (!COLLECT) continue;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -557,11 +566,10 @@ __device__ __forceinline__ uint32_t write_row(const StdParams& sp, const void* r
                 if constexpr (DT == SV_BF16) {
                     const uint4 w = make_uint4(bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16),
                                                bits[4] | (bits[5] << 16), bits[6] | (bits[7] << 16));
-                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(orow) + g * 8) = w;
+                    store16(static_cast<uint16_t*>(orow) + g * 8, w);
                 } else {
-                    uint4* o = reinterpret_cast<uint4*>(static_cast<uint32_t*>(orow) + g * 8);
-                    o[0] = make_uint4(bits[0], bits[1], bits[2], bits[3]);
-                    o[1] = make_uint4(bits[4], bits[5], bits[6], bits[7]);
+                    store16(static_cast<uint32_t*>(orow) + g * 8, make_uint4(bits[0], bits[1], bits[2], bits[3]));
+                    store16(static_cast<uint32_t*>(orow) + g * 8 + 4, make_uint4(bits[4], bits[5], bits[6], bits[7]));
                 }
             } else {
 #pragma unroll
