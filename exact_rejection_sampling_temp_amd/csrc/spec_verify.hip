@@ -285,6 +285,40 @@ __device__ __forceinline__ double wave_incl_scan(double v)
 }
 __device__ __forceinline__ int first_lane(uint64_t ballot) { return ballot ? __builtin_ctzll(ballot) : -1; }
 
+// The same sum and scan with DPP lane moves instead of LDS permutes, for
+// the single-wave, latency-bound draw finish (each step is a few cycles
+// instead of a round trip through the LDS crossbar).  The double moves as
+// two 32-bit halves; lanes without a source read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ double dpp_d(double v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, false);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_sum_dpp(double v)
+{
+    v += dpp_d<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_d<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_d<0x141>(v);  // row_half_mirror
+    v += dpp_d<0x140>(v);  // row_mirror: every lane holds its 16-lane row's sum
+    const double r0 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 0), __builtin_amdgcn_readlane(__double2loint(v), 0));
+    const double r1 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 16), __builtin_amdgcn_readlane(__double2loint(v), 16));
+    const double r2 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 32), __builtin_amdgcn_readlane(__double2loint(v), 32));
+    const double r3 = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 48), __builtin_amdgcn_readlane(__double2loint(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ double wave_incl_scan_dpp(double v)
+{
+    v += dpp_d<0x111>(v);        // row_shr:1
+    v += dpp_d<0x112>(v);        // row_shr:2
+    v += dpp_d<0x114>(v);        // row_shr:4
+    v += dpp_d<0x118>(v);        // row_shr:8: scans within each row
+    v += dpp_d<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_d<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
+
 // Block reductions over kThreads threads; every thread gets the result.
 // `sm` must hold kWaves entries and is free again on return.
 __device__ float block_max(float v, float* sm)
@@ -878,7 +912,7 @@ __device__ void finish_wave(const Params& p, int b)
 #pragma unroll
             for (int i = 0; i < 8; ++i) a += rE[i];
         }
-        const double S = wave_sum(a);
+        const double S = wave_sum_dpp(a);
         const double invS = 1.0 / S;  // p_v = e_v * invS (within an ulp of e_v / S)
         double zl = 0.0;
         if (resid) {
@@ -888,7 +922,7 @@ __device__ void finish_wave(const Params& p, int b)
                 for (int i = 0; i < 8; ++i) zl += fmax(0.0, rEA[i] * invS - p.len * rQA[i]);
             }
         }
-        Z = wave_sum(zl);
+        Z = wave_sum_dpp(zl);
         const bool use_resid = resid && Z > kResidEps;
         const double total = use_resid ? Z : S;
         const double target = ug * total;
@@ -903,7 +937,7 @@ __device__ void finish_wave(const Params& p, int b)
             double lt = 0.0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) lt += sub_weight(i);
-            const double incl = wave_incl_scan(lt);
+            const double incl = wave_incl_scan_dpp(lt);
             double excl = __shfl_up(incl, 1, 64);
             if (lane == 0) excl = 0.0;
             const int L = first_lane(__ballot(lt > 0.0 && carry + incl > target));
@@ -949,7 +983,7 @@ __device__ void finish_wave(const Params& p, int b)
                                      : 0.0;
                 lt += w[e];
             }
-            const double incl = wave_incl_scan(lt);
+            const double incl = wave_incl_scan_dpp(lt);
             double excl = __shfl_up(incl, 1, 64);
             if (lane == 0) excl = 0.0;
             const int L = first_lane(__ballot(lt > 0.0 && incl > rem));
