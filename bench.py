@@ -24,7 +24,11 @@ variant (spec_verify_lenient, l = 0.5) on the same inputs ("lenience").  A
 last leg runs the multi-step driver ("driver"): 256 streams of 64 tokens over
 c4-shaped position-only models, gamma* from the measured alpha at c = 0.05.
 "standardize" times sv_standardize (top-k k = 50, nucleus top_p = 0.9) over
-the 2 304 target rows of the c4 batch.
+the 2 304 target rows of the c4 batch.  "configs" times the other
+configurations one call at a time (c1, c2, c3 in sample and greedy mode,
+c5), each call after a write that evicts the caches: latency percentiles,
+tokens/s and achieved algorithmic GB/s (they are parity cases, not the
+headline workload).
 """
 from __future__ import annotations
 
@@ -117,6 +121,8 @@ def main():
                     help="tokens per stream of the multi-step driver leg (0 = skip)")
     ap.add_argument("--std-steps", type=int, default=20,
                     help="timed calls of each standardisation (0 = skip)")
+    ap.add_argument("--cfg-calls", type=int, default=50,
+                    help="timed calls per config of the per-config leg, c1, c2, c3 (sample and greedy), c5 (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -336,6 +342,63 @@ def main():
             stdz[name] = {"ms_per_call": ms, "alg_bytes": rows_bytes,
                           "achieved_GBps": rows_bytes / (ms * 1e-3) / 1e9}
 
+    cfgs = None
+    if args.cfg_calls > 0:
+        # the other configurations, each call timed alone between HIP events
+        # after a 512 MB write that evicts L2 and the last-level cache
+        # (outside the timed region); median / p10 / p90 over the calls
+        print("[bench] per-config leg", file=sys.stderr, flush=True)
+        flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        hev.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        cfgs = []
+        for cname, mode in (("c1", "sample"), ("c2", "sample"), ("c3", "sample"), ("c3", "greedy"), ("c5", "sample")):
+            hc = synth.make_inputs(cname, args.seed)
+            xc = to_device(hc, dev)
+            Bc, G1c, Vc = hc["target_logits"].shape
+            gc = G1c - 1
+            sp_c = hc["target_logits"].itemsize
+            sq_c = hc["draft_probs"].itemsize
+            smp = mode == "sample"
+            nc = torch.empty(Bc, dtype=torch.int32, device=dev)
+            oc = torch.empty((Bc, G1c), dtype=torch.int32, device=dev)
+            wsc = torch.zeros(sv.sv_workspace_bytes(Bc, gc, Vc), dtype=torch.uint8, device=dev)
+
+            def call_c(ev=None):
+                sv.spec_verify(xc["target_logits"], xc["draft_probs"] if smp else None, xc["draft_tokens"],
+                               xc["uniforms"] if smp else None, hc["temperature"], mode, n_accepted=nc,
+                               out_tokens=oc, workspace=wsc, events=ev, stream=stream)
+            for _ in range(5):
+                call_c()
+            torch.cuda.synchronize()
+            nb = nc.cpu().numpy().astype(np.int64)
+            evc = [(hev.create(), hev.create(), hev.create()) for _ in range(args.cfg_calls)]
+            for i in range(args.cfg_calls):
+                flush.fill_(float(i))
+                call_c(evc[i])
+            torch.cuda.synchronize()
+            ms_c = np.array([hev.elapsed_ms(e[0], e[2]) for e in evc])
+            for e in evc:
+                for hh in e:
+                    hev.destroy(hh)
+            # algorithmic bytes, early exit: target rows 0..n_b; in sample
+            # mode also the gathers of p and q at the drafts and the draft's
+            # row n_b when n_b < gamma
+            alg_c = float(((nb + 1) * Vc * sp_c).sum())
+            if smp:
+                alg_c += float(Bc * gc * (sp_c + sq_c) + ((nb < gc) * Vc * sq_c).sum())
+            med = float(np.median(ms_c))
+            cfgs.append({"config": cname, "mode": mode, "batch": int(Bc), "gamma": int(gc), "vocab": int(Vc),
+                         "logits_dtype": "bf16" if sp_c == 2 else "fp32",
+                         "probs_dtype": "bf16" if sq_c == 2 else "fp32", "calls": args.cfg_calls,
+                         "median_ms": med, "p10_ms": float(np.percentile(ms_c, 10)),
+                         "p90_ms": float(np.percentile(ms_c, 90)), "seqs_per_s": Bc / (med * 1e-3),
+                         "tokens_per_s": float((nb + 1).sum()) / (med * 1e-3),
+                         "mean_tokens_per_sequence": float((nb + 1).mean()), "alg_bytes": alg_c,
+                         "achieved_GBps": alg_c / (med * 1e-3) / 1e9,
+                         "frac": alg_c / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS})
+            del xc, wsc
+        del flush
+
     cpu = None
     if args.cpu_seconds > 0:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -372,6 +435,7 @@ def main():
         "lenience": lenl,
         "driver": drv,
         "standardize": stdz,
+        "configs": cfgs,
     }
     print(json.dumps(line), flush=True)
 

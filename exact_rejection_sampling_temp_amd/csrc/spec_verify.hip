@@ -1605,6 +1605,187 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
     if (i < ntail) tail[i] = 0;
 }
 
+// ------------------------------------------------------- small vocabularies
+
+// Rows of at most kSmallV entries: one wave verifies a whole sequence in a
+// single launch -- row statistics, the acceptance walk, the draw and the
+// outputs ([FI] Algorithm 1, Phases 3 and 4; [PB] section 3; [ST]) -- with
+// entry v of a row in lane v % 64, register v / 64, so a row is one
+// coalesced load per register and index order is (register, lane).  Every
+// e_v = 2^((z_v - m) log2(e)/T) is fp64 here, so S and p(x) are exact to
+// rounding.  The many-workgroup path above would spend a workgroup per row
+// chunk on a few entries.  Telemetry calls take that path.
+constexpr int kSmallK = 8;              // entries per lane
+constexpr int kSmallV = 64 * kSmallK;   // 512
+
+template <int DT>
+__device__ __forceinline__ float elem_at(const void* row, int64_t i)
+{
+    if constexpr (DT == SV_BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(row)[i] << 16);
+    else return static_cast<const float*>(row)[i];
+}
+
+template <int DT, int PT, bool GREEDY>
+__global__ __launch_bounds__(kThreads) void k_small(const Params p)
+{
+    const int lane = threadIdx.x & 63;
+    const int b = (int)(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (b >= p.B) return;  // a whole wave: there is no barrier in this kernel
+    const int G1 = p.gamma + 1;
+    const int V = p.V;
+    int32_t tok = 0;
+    float ul = 0.0f;
+    if (lane < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + lane];
+    if (!GREEDY && lane < G1) ul = p.uniforms[(int64_t)b * G1 + lane];
+    const bool invalid = __ballot(lane < p.gamma && (tok < 0 || tok >= V)) != 0;
+
+    // lane i keeps row i's statistics for the outputs
+    float st_m = NAN;
+    double st_S = NAN, st_P = NAN, st_Q = NAN;
+    int n = p.gamma, t = -1;
+    double Z = NAN;
+    if (!invalid) {
+        float z[kSmallK];
+        double e[kSmallK];
+        double S = 0.0;
+        for (int i = 0; i <= p.gamma; ++i) {
+            const void* zrow = static_cast<const char*>(p.logits) +
+                               (size_t)((int64_t)b * G1 + i) * V * (DT == SV_BF16 ? 2 : 4);
+            float m = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < kSmallK; ++j) {
+                const int v = lane + 64 * j;
+                z[j] = v < V ? elem_at<DT>(zrow, v) : -INFINITY;
+                m = fmaxf(m, z[j]);
+            }
+            m = wave_max(m);
+            if (lane == i) st_m = m;
+            if constexpr (GREEDY) {
+                // [FI] "Standardized Sampling", argmax case: the first index
+                // attaining the maximum; the draft survives iff it is that index
+                int a = INT_MAX;
+#pragma unroll
+                for (int j = kSmallK - 1; j >= 0; --j)
+                    if (lane + 64 * j < V && z[j] == m) a = lane + 64 * j;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o, 64));
+                if (i == p.gamma || __shfl(tok, i, 64) != a) {
+                    n = i;
+                    t = a;
+                    break;
+                }
+            } else {
+                const double nMcd = -(double)m * p.cd;
+                double es = 0.0;
+#pragma unroll
+                for (int j = 0; j < kSmallK; ++j) {
+                    e[j] = lane + 64 * j < V ? exp2_f64(fma((double)z[j], p.cd, nMcd), p.ex) : 0.0;
+                    es += e[j];
+                }
+                S = wave_sum_dpp(es);
+                if (lane == i) st_S = S;
+                if (i == p.gamma) break;  // every draft accepted: row gamma is the bonus row
+                const int x = __shfl(tok, i, 64);
+                const float zx = elem_at<DT>(zrow, x);
+                const double P = zx > -INFINITY ? exp2(((double)zx - (double)m) * p.cd) / S : 0.0;
+                const void* qrow = static_cast<const char*>(p.probs) +
+                                   (size_t)((int64_t)b * p.gamma + i) * V * (PT == SV_BF16 ? 2 : 4);
+                const double Q = (double)elem_at<PT>(qrow, x);
+                if (lane == i) { st_P = P; st_Q = Q; }
+                // accept iff u <= min(1, p / q), q scaled by the lenience; q <= 0 accepts
+                const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / (p.len * Q));
+                if (!((double)__shfl(ul, i, 64) <= thr)) {
+                    n = i;
+                    break;
+                }
+            }
+        }
+        if constexpr (!GREEDY) {
+            // the draw from row n (e and S of that row are in registers):
+            // norm(max(0, p - l q)) after a rejection, p itself when that mass
+            // is at most 1e-15 or every draft was accepted
+            const bool resid = n < p.gamma;
+            const double invS = 1.0 / S;
+            double w[kSmallK];
+            if (resid) {
+                const void* qrow = static_cast<const char*>(p.probs) +
+                                   (size_t)((int64_t)b * p.gamma + n) * V * (PT == SV_BF16 ? 2 : 4);
+                double zs = 0.0;
+#pragma unroll
+                for (int j = 0; j < kSmallK; ++j) {
+                    const int v = lane + 64 * j;
+                    const double q = v < V ? (double)elem_at<PT>(qrow, v) : 0.0;
+                    w[j] = v < V ? fmax(0.0, e[j] * invS - p.len * q) : 0.0;
+                    zs += w[j];
+                }
+                Z = wave_sum_dpp(zs);
+            }
+            const bool use_resid = resid && Z > kResidEps;
+            if (!use_resid) {
+#pragma unroll
+                for (int j = 0; j < kSmallK; ++j) w[j] = e[j];
+            }
+            const double target = (double)__shfl(ul, p.gamma, 64) * (use_resid ? Z : S);
+            // smallest index whose running weight (index order) exceeds the target
+            double carry = 0.0;
+#pragma unroll
+            for (int j = 0; j < kSmallK; ++j) {
+                if (t >= 0) break;
+                const double incl = wave_incl_scan_dpp(w[j]);
+                const int L = first_lane(__ballot(w[j] > 0.0 && carry + incl > target));
+                if (L >= 0) t = L + 64 * j;
+                else carry += __shfl(incl, 63, 64);
+            }
+            if (t < 0) {
+                // u * total at or past the end (only by rounding): the last positive weight
+                int last = -1;
+#pragma unroll
+                for (int j = 0; j < kSmallK; ++j)
+                    if (w[j] > 0.0) last = lane + 64 * j;
+                t = wave_max_i(last);
+            }
+            if (!resid) Z = NAN;
+        }
+    }
+
+    if (lane < G1) {
+        int32_t o;
+        if (invalid) o = -1;
+        else if (lane < n) o = tok;
+        else if (lane == n) o = t;
+        else o = -1;
+        p.tok_out[(int64_t)b * G1 + lane] = o;
+        const bool row_seen = !invalid && lane <= n;
+        if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + lane] = row_seen ? st_m : NAN;
+        if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + lane] = row_seen && !GREEDY ? st_S : NAN;
+        if (lane < p.gamma) {
+            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + lane] = row_seen && !GREEDY ? st_P : NAN;
+            if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + lane] = row_seen && !GREEDY ? st_Q : NAN;
+        }
+    }
+    if (lane == 0) {
+        p.n_out[b] = invalid ? -1 : n;
+        if (p.aux_resid) p.aux_resid[b] = invalid || GREEDY ? NAN : Z;
+    }
+}
+
+template <int DT, int PT>
+bool launch_small_t(bool greedy, const Params& p, hipStream_t s)
+{
+    const dim3 grid((unsigned)((p.B + kWaves - 1) / kWaves));
+    if (greedy) hipLaunchKernelGGL((k_small<DT, DT, true>), grid, dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_small<DT, PT, false>), grid, dim3(kThreads), 0, s, p);
+    return hipGetLastError() == hipSuccess;
+}
+
+bool launch_small(int dt, int pt, bool greedy, const Params& p, hipStream_t s)
+{
+    if (dt == SV_FP32 && (greedy || pt == SV_FP32)) return launch_small_t<SV_FP32, SV_FP32>(greedy, p, s);
+    if (dt == SV_FP32) return launch_small_t<SV_FP32, SV_BF16>(greedy, p, s);
+    if (greedy || pt == SV_FP32) return launch_small_t<SV_BF16, SV_FP32>(greedy, p, s);
+    return launch_small_t<SV_BF16, SV_BF16>(greedy, p, s);
+}
+
 // ---------------------------------------------------------------- host dispatch
 
 template <int DT, int PT>
@@ -1793,7 +1974,11 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)
         return SV_ERR_LAUNCH;
     bool ok;
-    if (greedy) {
+    if (vocab <= kSmallV && !tele) {
+        // one launch, one wave per sequence (the workspace is not touched)
+        ok = launch_small(logits_dtype, probs_dtype, greedy, p, s);
+        if (ok && ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) ok = false;
+    } else if (greedy) {
         ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)grid1, batch, p, s, ev_mid)
                                      : launch_greedy_t<SV_FP32>(vec, (int)grid1, batch, p, s, ev_mid);
     } else {
