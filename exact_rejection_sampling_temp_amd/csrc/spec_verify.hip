@@ -1625,6 +1625,35 @@ __device__ __forceinline__ float elem_at(const void* row, int64_t i)
     else return static_cast<const float*>(row)[i];
 }
 
+// max / min over the wave with DPP moves and four row read-outs (see
+// wave_sum_dpp)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ int wave_min_i_dpp(int v)
+{
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 template <int DT, int PT, bool GREEDY>
 __global__ __launch_bounds__(kThreads) void k_small(const Params p)
 {
@@ -1633,6 +1662,7 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
     if (b >= p.B) return;  // a whole wave: there is no barrier in this kernel
     const int G1 = p.gamma + 1;
     const int V = p.V;
+    const int KV = (V + 63) / 64;  // registers that hold entries (wave-uniform): the rest is skipped
     int32_t tok = 0;
     float ul = 0.0f;
     if (lane < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + lane];
@@ -1655,10 +1685,10 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
 #pragma unroll
             for (int j = 0; j < kSmallK; ++j) {
                 const int v = lane + 64 * j;
-                z[j] = v < V ? elem_at<DT>(zrow, v) : -INFINITY;
+                z[j] = j < KV && v < V ? elem_at<DT>(zrow, v) : -INFINITY;
                 m = fmaxf(m, z[j]);
             }
-            m = wave_max(m);
+            m = wave_max_dpp(m);
             if (lane == i) st_m = m;
             if constexpr (GREEDY) {
                 // [FI] "Standardized Sampling", argmax case: the first index
@@ -1666,9 +1696,8 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
                 int a = INT_MAX;
 #pragma unroll
                 for (int j = kSmallK - 1; j >= 0; --j)
-                    if (lane + 64 * j < V && z[j] == m) a = lane + 64 * j;
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) a = min(a, __shfl_xor(a, o, 64));
+                    if (j < KV && lane + 64 * j < V && z[j] == m) a = lane + 64 * j;
+                a = wave_min_i_dpp(a);
                 if (i == p.gamma || __shfl(tok, i, 64) != a) {
                     n = i;
                     t = a;
@@ -1679,8 +1708,11 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
                 double es = 0.0;
 #pragma unroll
                 for (int j = 0; j < kSmallK; ++j) {
-                    e[j] = lane + 64 * j < V ? exp2_f64(fma((double)z[j], p.cd, nMcd), p.ex) : 0.0;
-                    es += e[j];
+                    e[j] = 0.0;
+                    if (j < KV) {
+                        if (lane + 64 * j < V) e[j] = exp2_f64(fma((double)z[j], p.cd, nMcd), p.ex);
+                        es += e[j];
+                    }
                 }
                 S = wave_sum_dpp(es);
                 if (lane == i) st_S = S;
@@ -1714,9 +1746,11 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
 #pragma unroll
                 for (int j = 0; j < kSmallK; ++j) {
                     const int v = lane + 64 * j;
-                    const double q = v < V ? (double)elem_at<PT>(qrow, v) : 0.0;
-                    w[j] = v < V ? fmax(0.0, e[j] * invS - p.len * q) : 0.0;
-                    zs += w[j];
+                    w[j] = 0.0;
+                    if (j < KV) {
+                        if (v < V) w[j] = fmax(0.0, e[j] * invS - p.len * (double)elem_at<PT>(qrow, v));
+                        zs += w[j];
+                    }
                 }
                 Z = wave_sum_dpp(zs);
             }
@@ -1730,7 +1764,7 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
             double carry = 0.0;
 #pragma unroll
             for (int j = 0; j < kSmallK; ++j) {
-                if (t >= 0) break;
+                if (t >= 0 || j >= KV) break;
                 const double incl = wave_incl_scan_dpp(w[j]);
                 const int L = first_lane(__ballot(w[j] > 0.0 && carry + incl > target));
                 if (L >= 0) t = L + 64 * j;
