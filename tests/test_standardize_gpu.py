@@ -151,3 +151,30 @@ def test_bf16_long_tie_runs(method, kw):
     rng = np.random.default_rng(13)
     z = np.round(rng.standard_normal((6, 150_000))).astype(np.float32)
     _check(synth.f32_to_bf16_bits(z), method, **kw)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_degenerate_rows(dt):
+    """Rows of -inf only, a single finite entry among -inf, half -inf,
+    one-entry rows, and k at 1, 2, V - 1, V and past V."""
+    rng = np.random.default_rng(14)
+    V = 4096
+    z = (rng.standard_normal((6, V)) * 2).astype(np.float32)
+    z[0] = -np.inf                      # no finite entry
+    z[1] = -np.inf
+    z[1, 1234] = 0.75                   # one finite entry
+    z[2, :V // 2] = -np.inf
+    zz = synth.f32_to_bf16_bits(z) if dt == "bf16" else z
+    for k in (1, 2, V - 1):
+        _check(zz, "topk", k=k)
+    for k in (V, V + 5):                # the whole row
+        assert np.array_equal(_gpu_std(zz, "topk", k=k), zz)
+    for top_p in (0.5, 0.999):
+        _check(zz[1:], "topp", top_p=top_p)
+        # no finite entry: no mass to reach top_p, every entry stays
+        assert np.array_equal(_gpu_std(zz[:1], "topp", top_p=top_p), zz[:1])
+    one = np.ascontiguousarray(zz[1:, :1])
+    for k in (1, 3):
+        assert np.array_equal(_gpu_std(one, "topk", k=k), one)
+    finite = one[np.isfinite(synth.bf16_bits_to_f32(one) if dt == "bf16" else one)[:, 0]]
+    _check(finite, "topp", top_p=0.5)
