@@ -422,6 +422,8 @@ def main():
                    "batch": int(B), "gamma": int(gamma), "vocab": int(V), "input_dtype": "bf16"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     # the measured bytes (calibrated FETCH_SIZE + WRITE_SIZE of this source) over the same time
+                     "traffic_GBps": None if traffic is None else traffic / (call_ms * 1e-3) / 1e9,
                      "kernel": "spec_verify call: k_main_sample + k_rest_sample",
                      "alg_bytes_per_launch": call_alg_bytes, "avg_launch_ms": call_ms},
         "cpu_baseline": cpu,
