@@ -7,10 +7,13 @@ probabilities, T=1.0; synthetic inputs, resident in HBM before timing).
 Two input sets generated with different seeds alternate between steps, so
 one step never finds the previous step's rows in the 256 MB last-level cache.
 
-Prints one JSON line: verified sequences/s (value), the roofline of the
-call (achieved algorithmic GB/s from HIP events recorded on the call's stream
-around its launches, against 8 TB/s), and the fp64 CPU oracle timed on this
-host's cores on the same inputs.  The call is one row-stage launch that also
+Prints one JSON line: verified sequences/s (value, wall clock over the
+timed steps), the roofline of the call (achieved algorithmic GB/s: bytes per
+call over the mean call time, from two HIP events recorded on the call's
+stream around the timed steps, against 8 TB/s), and the fp64 CPU oracle timed
+on this host's cores on the same inputs.  The timed steps run back to back
+with no event between them; the split of a call between its two launches
+("stages_ms") comes from a separate pass with events around every launch.  The call is one row-stage launch that also
 streams most of the draw (k_main_sample) and a short launch that finishes
 the draw (k_rest_sample); the row and draw work share the first launch, so
 the roofline covers the whole call.
@@ -47,6 +50,7 @@ METRIC = "verified seqs/sec + achieved HBM GB/s (% of peak) at B=256, gamma=8, V
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_call_c4.json")
 KERNEL_SRC = os.path.join(ROOT, "exact_rejection_sampling_temp_amd", "csrc", "spec_verify.hip")
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
 class HipEvents:
@@ -56,15 +60,26 @@ class HipEvents:
         import torch  # noqa: F401
         self.lib = ctypes.CDLL("libamdhip64.so.7")
         self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
     def create(self):
+        # timing-only events (hipEventDisableSystemFence): recording one does
+        # not write back and invalidate the caches, which would cost a few
+        # microseconds and slow the work around it; elapsed times are read
+        # after a stream synchronisation, so no fence is needed
         e = ctypes.c_void_p()
-        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        rc = self.lib.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed ({rc})")
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         return e.value
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -108,7 +123,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps before the timed ones (200 x ~0.11 ms lets the GPU clocks settle)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=2.0,
                     help="minimum wall time of the CPU-oracle baseline (0 = skip)")
@@ -169,14 +185,29 @@ def main():
     torch.cuda.synchronize()
 
     hev = HipEvents()
-    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(args.steps)]
+    # the timed region: the steps back to back, one event pair around all of
+    # them on the call's stream (events between the calls would add their
+    # own cost to every call)
+    eb, ee = hev.create(), hev.create()
     print("[bench] timed steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    hev.record(eb, stream)
     for i in range(args.steps):
-        step(i, events=evs[i])
+        step(i)
+    hev.record(ee, stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    call_ms = hev.elapsed_ms(eb, ee) / args.steps
+    hev.destroy(eb)
+    hev.destroy(ee)
+    # the split between the two launches, from a separate untimed pass with
+    # events before, between and after the launches of every call
+    nsplit = min(args.steps, 50)
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(nsplit)]
+    for i in range(nsplit):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
     rows_ms = [hev.elapsed_ms(e[0], e[1]) for e in evs]
     draw_ms = [hev.elapsed_ms(e[1], e[2]) for e in evs]
     for e in evs:
@@ -197,7 +228,6 @@ def main():
     draw_bytes = [float((V * s_p + (n < gamma) * V * s_q).sum()) for n in n_sets]
     mean_rows_ms = float(np.mean(rows_ms))
     mean_draw_ms = float(np.mean(draw_ms))
-    call_ms = mean_rows_ms + mean_draw_ms
     rows_alg_bytes = float(np.mean([rows_bytes[i % 2] for i in range(args.steps)]))
     draw_alg_bytes = float(np.mean([draw_bytes[i % 2] for i in range(args.steps)]))
     call_alg_bytes = rows_alg_bytes + draw_alg_bytes
@@ -228,12 +258,16 @@ def main():
         for i in range(4):
             tstep(i)
         torch.cuda.synchronize()
-        tev = [(hev.create(), hev.create(), hev.create(), hev.create()) for _ in range(args.tele_steps)]
         t1 = time.perf_counter()
         for i in range(args.tele_steps):
-            tstep(i, events=tev[i])
+            tstep(i)
         torch.cuda.synchronize()
         tel = time.perf_counter() - t1
+        # stage split: a separate pass with events around each stage
+        tev = [(hev.create(), hev.create(), hev.create(), hev.create()) for _ in range(min(args.tele_steps, 20))]
+        for i in range(len(tev)):
+            tstep(i, events=tev[i])
+        torch.cuda.synchronize()
         t_main = float(np.mean([hev.elapsed_ms(e[0], e[1]) for e in tev]))
         t_sweep = float(np.mean([hev.elapsed_ms(e[1], e[3]) for e in tev]))
         t_rest = float(np.mean([hev.elapsed_ms(e[3], e[2]) for e in tev]))
@@ -251,7 +285,7 @@ def main():
             "steps": args.tele_steps, "ms_per_step": tcall_ms, "seqs_per_s": B * args.tele_steps / tel,
             "stages_ms": {"main_all_rows": t_main, "sweep": t_sweep, "rest": t_rest},
             "alg_bytes_per_call": tcall_b,
-            "achieved_GBps": tcall_b / ((t_main + t_sweep + t_rest) * 1e-3) / 1e9,
+            "achieved_GBps": tcall_b / (tcall_ms * 1e-3) / 1e9,
             "sweep_roofline": {"bound": "hbm", "achieved": sweep_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                "frac": sweep_gbps / HBM_PEAK_GBPS, "kernel": "k_beta + k_beta_merge",
                                "alg_bytes_per_launch": sweep_b, "avg_launch_ms": t_sweep},
@@ -276,16 +310,17 @@ def main():
         for i in range(4):
             lstep(i)
         torch.cuda.synchronize()
-        lev = [(hev.create(), hev.create(), hev.create()) for _ in range(args.len_steps)]
+        lb, le = hev.create(), hev.create()
         t2 = time.perf_counter()
+        hev.record(lb, stream)
         for i in range(args.len_steps):
-            lstep(i, events=lev[i])
+            lstep(i)
+        hev.record(le, stream)
         torch.cuda.synchronize()
         lel = time.perf_counter() - t2
-        l_call = float(np.mean([hev.elapsed_ms(e[0], e[2]) for e in lev]))
-        for e in lev:
-            for h in e:
-                hev.destroy(h)
+        l_call = hev.elapsed_ms(lb, le) / args.len_steps
+        hev.destroy(lb)
+        hev.destroy(le)
         l_bytes = float(np.mean([((n + 1) * V * s_p).sum() + B * gamma * (s_p + s_q)
                                  + (V * s_p + (n < gamma) * V * s_q).sum() for n in ln_sets]))
         lenl = {"lenience": args.lenience, "steps": args.len_steps, "ms_per_step": 1e3 * lel / args.len_steps,
@@ -330,11 +365,10 @@ def main():
                 sv.standardize(zrows, out=zout, stream=stream, **kw)
             torch.cuda.synchronize()
             e0, e1 = hev.create(), hev.create()
-            hev.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-            hev.lib.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
+            hev.record(e0, stream)
             for _ in range(args.std_steps):
                 sv.standardize(zrows, out=zout, stream=stream, **kw)
-            hev.lib.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
+            hev.record(e1, stream)
             torch.cuda.synchronize()
             ms = hev.elapsed_ms(e0, e1) / args.std_steps
             hev.destroy(e0)
@@ -349,7 +383,6 @@ def main():
         # (outside the timed region); median / p10 / p90 over the calls
         print("[bench] per-config leg", file=sys.stderr, flush=True)
         flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
-        hev.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         cfgs = []
         for cname, mode in (("c1", "sample"), ("c2", "sample"), ("c3", "sample"), ("c3", "greedy"), ("c5", "sample")):
             hc = synth.make_inputs(cname, args.seed)
@@ -371,15 +404,15 @@ def main():
                 call_c()
             torch.cuda.synchronize()
             nb = nc.cpu().numpy().astype(np.int64)
-            evc = [(hev.create(), hev.create(), hev.create()) for _ in range(args.cfg_calls)]
+            evc = [(hev.create(), None, hev.create()) for _ in range(args.cfg_calls)]
             for i in range(args.cfg_calls):
                 flush.fill_(float(i))
                 call_c(evc[i])
             torch.cuda.synchronize()
             ms_c = np.array([hev.elapsed_ms(e[0], e[2]) for e in evc])
             for e in evc:
-                for hh in e:
-                    hev.destroy(hh)
+                hev.destroy(e[0])
+                hev.destroy(e[2])
             # algorithmic bytes, early exit: target rows 0..n_b; in sample
             # mode also the gathers of p and q at the drafts and the draft's
             # row n_b when n_b < gamma
