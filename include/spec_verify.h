@@ -87,7 +87,8 @@ typedef struct {
     /* hipEvent_t handles recorded on `stream`: before the first launch,
      * after the first launch (the row stage, which in sample mode also
      * streams most of the draw), and after the last launch.  Any may be
-     * NULL. */
+     * NULL.  For V <= 512 without telemetry the call is a single launch (one
+     * wave per sequence), and ev_mid is recorded after it, like ev_end. */
     void* ev_begin;
     void* ev_mid;
     void* ev_end;
@@ -141,7 +142,8 @@ int sv_workspace_init(void* workspace, size_t bytes, void* stream);
  *   workspace             device buffer of >= sv_workspace_bytes(B, gamma, V)
  *                         bytes, 256-byte aligned, zero-filled before first use
  *                         (sv_workspace_init); calls that overlap on the same
- *                         workspace race
+ *                         workspace race.  (Always checked; the single-launch
+ *                         path for V <= 512 does not touch it.)
  *   extras                optional outputs / timing events, or NULL
  *   stream                hipStream_t to enqueue on
  *
