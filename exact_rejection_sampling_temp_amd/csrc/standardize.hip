@@ -79,7 +79,6 @@ constexpr int unroll_of() { return VEC ? (DT == SV_BF16 ? kUnroll : kUnroll / 2)
 constexpr int kHThreads = 1024;
 constexpr int kHWaves = kHThreads / 64;
 constexpr int kHWords = 32768;                      // 65 536 16-bit counters
-constexpr int kHKeysPerThread = 65536 / kHThreads;  // 64
 constexpr uint32_t kTieCap = 1024;                  // listed ties per wave (64 KiB of the histogram's space)
 
 struct StdParams {
@@ -679,7 +678,7 @@ __global__ __launch_bounds__(kHThreads) void k_standardize_b16(const StdParams s
         const uint32_t key_hi = 65535u - 64u * (uint32_t)tid;
         uint32_t c_loc = 0, top_loc = 0;
 #pragma unroll
-        for (int j = 63; j >= 0; --j) {
+        for (int j = 65536 / kHThreads - 1; j >= 0; --j) {  // 64 keys per thread
             const uint32_t n = cnt_at(j);
             c_loc += n;
             if (n) top_loc = key_hi - (uint32_t)j;
