@@ -5,8 +5,6 @@ from __future__ import annotations
 
 import numpy as np
 
-import oracle
-
 
 def to_device(d: dict, device="cuda"):
     import torch
@@ -65,6 +63,7 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
 
 
 def run_ref(d: dict, mode: str = "sample", telemetry: bool = False, lenience: float = 1.0):
+    import oracle  # here, not at module level: bench.py takes to_device from this module
     if mode == "greedy":
         return oracle.spec_verify_ref(d["target_logits"], None, d["draft_tokens"], None, 1.0, oracle.GREEDY)
     return oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
