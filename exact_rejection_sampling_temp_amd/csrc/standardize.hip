@@ -269,6 +269,34 @@ __device__ __forceinline__ T block_excl_scan(T v, T* sm, T* total)
     return before + incl - v;
 }
 
+// block_excl_scan of a count and a mass together (one pair of barriers).
+__device__ __forceinline__ void block_excl_scan2(uint32_t c, double m, uint32_t* smu, double* smd, uint32_t* c_before,
+                                                 double* m_before, uint32_t* c_total, double* m_total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int nw = (int)(blockDim.x >> 6);
+    const uint32_t ci = wave_incl_scan_t(c);
+    const double mi = wave_incl_scan_t(m);
+    if (lane == 63) { smu[w] = ci; smd[w] = mi; }
+    __syncthreads();
+    uint32_t cb = 0, ca = 0;
+    double mb = 0.0, ma = 0.0;
+#pragma unroll
+    for (int i = 0; i < kMaxWaves; ++i) {
+        if (i >= nw) break;
+        const uint32_t sc = smu[i];
+        const double sd = smd[i];
+        if (i < w) { cb += sc; mb += sd; }
+        ca += sc;
+        ma += sd;
+    }
+    __syncthreads();
+    *c_before = cb + ci - c;
+    *m_before = mb + mi - m;
+    *c_total = ca;
+    *m_total = ma;
+}
+
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sm)
 {
 #pragma unroll
@@ -290,6 +318,7 @@ struct StdSmall {
     double above_mass;
     uint32_t tcross, cb;  // the thread whose keys hold the crossing, and the count above them
     double mb;            // the mass above them
+    uint32_t kmax[kMaxWaves];  // bf16 kernel: each wave's largest key (the row maximum)
 };
 
 // The selection's result for one row.
@@ -637,6 +666,7 @@ __global__ __launch_bounds__(kHThreads) void k_standardize_b16(const StdParams s
         for (int i = tid; i < kHWords / 4; i += kHThreads) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
         auto count_key = [&](uint32_t key) { atomicAdd(&hist[key >> 1], (key & 1u) ? 0x10000u : 1u); };
+        uint32_t kmax2 = 0, kmax1 = 0;  // nucleus: the largest key seen (packed pairs, single entries)
         for (int j0 = run.g_begin; j0 < run.g_end; j0 += U * 64) {  // uniform trip count
             G8 gu[U];
 #pragma unroll
@@ -654,11 +684,24 @@ __global__ __launch_bounds__(kHThreads) void k_standardize_b16(const StdParams s
                         const uint32_t k2 = keys2(word_of(gu[u].a, i));
                         count_key(k2 & 0xffffu);
                         count_key(k2 >> 16);
+                        if (NUCLEUS)
+                            kmax2 = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, kmax2),
+                                                                                          __builtin_bit_cast(u16x2, k2)));
                     }
                 } else {
-                    for (int e = 0; g * 8 + e < V; ++e) count_key(key_of<SV_BF16>(bits_of<SV_BF16>(gu[u], e)));
+                    for (int e = 0; g * 8 + e < V; ++e) {
+                        const uint32_t key = key_of<SV_BF16>(bits_of<SV_BF16>(gu[u], e));
+                        count_key(key);
+                        kmax1 = max(kmax1, key);
+                    }
                 }
             }
+        }
+        if (NUCLEUS) {
+            uint32_t km = max(max(kmax2 & 0xffffu, kmax2 >> 16), kmax1);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, 64));
+            if (lane == 0) sm.kmax[tid >> 6] = km;  // published by the barrier below
         }
         __syncthreads();
 
@@ -676,16 +719,16 @@ __global__ __launch_bounds__(kHThreads) void k_standardize_b16(const StdParams s
             return (j & 1) ? (w & 0xffffu) : (w >> 16);
         };
         const uint32_t key_hi = 65535u - 64u * (uint32_t)tid;
-        uint32_t c_loc = 0, top_loc = 0;
+        uint32_t c_loc = 0;
 #pragma unroll
-        for (int j = 65536 / kHThreads - 1; j >= 0; --j) {  // 64 keys per thread
-            const uint32_t n = cnt_at(j);
-            c_loc += n;
-            if (n) top_loc = key_hi - (uint32_t)j;
-        }
-        // the highest key present gives the row maximum
+        for (int j = 65536 / kHThreads - 1; j >= 0; --j) c_loc += cnt_at(j);  // 64 keys per thread
+        // the row maximum: the largest key the counting pass saw
         double m = 0.0;
-        if (NUCLEUS) m = (double)value_of_key<SV_BF16>(block_max_u32(top_loc, sm.u));
+        if (NUCLEUS) {
+            uint32_t km = 0;
+            for (int w = 0; w < kHWaves; ++w) km = max(km, sm.kmax[w]);
+            m = (double)value_of_key<SV_BF16>(km);
+        }
         auto mass_of = [&](uint32_t key, uint32_t n) -> double {
             const float z = value_of_key<SV_BF16>(key);
             return z > -INFINITY ? (double)n * exp2_fast(((double)z - m) * sp.cd) : 0.0;
@@ -711,10 +754,10 @@ __global__ __launch_bounds__(kHThreads) void k_standardize_b16(const StdParams s
             __syncthreads();
             m_loc = rmass[w_lo >> 5];
         }
-        uint32_t c_tot;
-        double m_tot = 0.0;
-        const uint32_t c_before = block_excl_scan<uint32_t>(c_loc, sm.u, &c_tot);
-        const double m_before = NUCLEUS ? block_excl_scan<double>(m_loc, sm.d, &m_tot) : 0.0;
+        uint32_t c_tot, c_before;
+        double m_tot = 0.0, m_before = 0.0;
+        if (NUCLEUS) block_excl_scan2(c_loc, m_loc, sm.u, sm.d, &c_before, &m_before, &c_tot, &m_tot);
+        else c_before = block_excl_scan<uint32_t>(c_loc, sm.u, &c_tot);
         if (c_tot != (uint32_t)V) {
             // some value occurs 65 536 times or more: a 16-bit counter wrapped
             __syncthreads();
