@@ -1804,9 +1804,164 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
     }
 }
 
+// Rows of at most 16 entries with gamma < 16 (c1: V = 8): one 16-lane DPP row
+// per sequence, four sequences per wave; entry v in lane v of the row.  The
+// same steps as k_small, with every reduction and scan kept inside the row
+// (quad swaps and mirrors, row_shr), and the four walks run in lockstep with
+// every lane active, each row masked once its walk has ended.
+constexpr int kTinyV = 16;
+
+__device__ __forceinline__ float row_max16(float v)
+{
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ int row_min16(int v)
+{
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false));
+    return min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));
+}
+__device__ __forceinline__ double row_sum16(double v)
+{
+    v += dpp_d<0xB1>(v);
+    v += dpp_d<0x4E>(v);
+    v += dpp_d<0x141>(v);
+    return v + dpp_d<0x140>(v);
+}
+__device__ __forceinline__ double row_incl_scan16(double v)
+{
+    v += dpp_d<0x111>(v);
+    v += dpp_d<0x112>(v);
+    v += dpp_d<0x114>(v);
+    return v + dpp_d<0x118>(v);
+}
+
+template <int DT, int PT, bool GREEDY>
+__global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane >> 4, l = lane & 15;  // row (sequence) of the wave, lane in the row
+    const int b = (int)((blockIdx.x * kWaves + (threadIdx.x >> 6)) * 4) + r;
+    const bool live = b < p.B;  // rows past the batch run along masked (no loads, no stores)
+    const int G1 = p.gamma + 1;
+    const int V = p.V;
+    const int base = lane & ~15;
+    int32_t tok = 0;
+    float ul = 0.0f;
+    if (live && l < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + l];
+    if (!GREEDY && live && l < G1) ul = p.uniforms[(int64_t)b * G1 + l];
+    const uint64_t bad = __ballot(live && l < p.gamma && (tok < 0 || tok >= V));
+    const bool invalid = ((bad >> (16 * r)) & 0xffffull) != 0ull;
+
+    float st_m = NAN;
+    double st_S = NAN, st_P = NAN, st_Q = NAN;
+    int n = p.gamma, t = -1;
+    double Z = NAN;
+    bool active = live && !invalid;  // this row's walk goes on
+    double e = 0.0, S = 0.0;
+    float z = -INFINITY;
+    for (int i = 0; i <= p.gamma; ++i) {
+        if (__ballot(active) == 0ull) break;
+        const void* zrow = static_cast<const char*>(p.logits) + (size_t)((int64_t)b * G1 + i) * V * (DT == SV_BF16 ? 2 : 4);
+        z = active && l < V ? elem_at<DT>(zrow, l) : -INFINITY;
+        const float m = row_max16(z);
+        if (active && l == i) st_m = m;
+        if constexpr (GREEDY) {
+            const int a = row_min16(l < V && z == m ? l : INT_MAX);
+            const bool stop = i == p.gamma || __shfl(tok, base + i, 64) != a;
+            if (active && stop) {
+                n = i;
+                t = a;
+                active = false;
+            }
+        } else {
+            // e and S keep row n's values once a row's walk has ended
+            const double ei = active && l < V ? exp2_f64(fma((double)z, p.cd, -(double)m * p.cd), p.ex) : 0.0;
+            const double Si = row_sum16(ei);
+            if (active) { e = ei; S = Si; }
+            if (active && l == i) st_S = Si;
+            if (i == p.gamma) break;  // the rows still walking accepted every draft
+            const int x = __shfl(tok, base + i, 64);
+            const float zx = __shfl(z, base + (x & 15), 64);  // (x < V <= 16 on an active row)
+            const float ui = __shfl(ul, base + i, 64);
+            double P = 0.0, Q = 0.0;
+            bool rej = false;
+            if (active) {
+                P = zx > -INFINITY ? exp2(((double)zx - (double)m) * p.cd) / Si : 0.0;
+                const void* qrow = static_cast<const char*>(p.probs) +
+                                   (size_t)((int64_t)b * p.gamma + i) * V * (PT == SV_BF16 ? 2 : 4);
+                Q = (double)elem_at<PT>(qrow, x);
+                const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / (p.len * Q));
+                rej = !((double)ui <= thr);
+            }
+            if (active && l == i) { st_P = P; st_Q = Q; }
+            if (active && rej) {
+                n = i;
+                active = false;
+            }
+        }
+    }
+    if constexpr (!GREEDY) {
+        // the draw of every row that walked (n and its e, S are this row's)
+        const bool walked = live && !invalid;
+        const bool resid = n < p.gamma;
+        double w = e;
+        double Zr = 0.0;
+        if (walked && resid) {
+            const void* qrow = static_cast<const char*>(p.probs) +
+                               (size_t)((int64_t)b * p.gamma + n) * V * (PT == SV_BF16 ? 2 : 4);
+            const double q = l < V ? (double)elem_at<PT>(qrow, l) : 0.0;
+            w = l < V ? fmax(0.0, e * (1.0 / S) - p.len * q) : 0.0;
+        }
+        if (!(walked && resid)) w = walked ? e : 0.0;
+        Zr = row_sum16(walked && resid ? w : 0.0);
+        const bool use_resid = walked && resid && Zr > kResidEps;
+        if (walked && resid && !use_resid) w = e;
+        const double total = use_resid ? Zr : S;
+        const double target = (double)__shfl(ul, base + p.gamma, 64) * total;
+        const double incl = row_incl_scan16(w);
+        const uint64_t hit = __ballot(walked && w > 0.0 && incl > target);
+        const uint32_t hr = (uint32_t)((hit >> (16 * r)) & 0xffffull);
+        const uint64_t pos = __ballot(walked && w > 0.0);
+        const uint32_t pr = (uint32_t)((pos >> (16 * r)) & 0xffffull);
+        if (walked) t = hr ? __builtin_ctz(hr) : (pr ? 31 - __builtin_clz(pr) : -1);
+        if (walked && resid) Z = Zr;
+    }
+
+    if (live && l < G1) {
+        int32_t o;
+        if (invalid) o = -1;
+        else if (l < n) o = tok;
+        else if (l == n) o = t;
+        else o = -1;
+        p.tok_out[(int64_t)b * G1 + l] = o;
+        const bool row_seen = !invalid && l <= n;
+        if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + l] = row_seen ? st_m : NAN;
+        if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + l] = row_seen && !GREEDY ? st_S : NAN;
+        if (l < p.gamma) {
+            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + l] = row_seen && !GREEDY ? st_P : NAN;
+            if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + l] = row_seen && !GREEDY ? st_Q : NAN;
+        }
+    }
+    if (live && l == 0) {
+        p.n_out[b] = invalid ? -1 : n;
+        if (p.aux_resid) p.aux_resid[b] = invalid || GREEDY ? NAN : Z;
+    }
+}
+
 template <int DT, int PT>
 bool launch_small_t(bool greedy, const Params& p, hipStream_t s)
 {
+    if (p.V <= kTinyV && p.gamma < 16) {
+        const dim3 grid((unsigned)((p.B + 4 * kWaves - 1) / (4 * kWaves)));  // four sequences per wave
+        if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_tiny<DT, PT, false>), grid, dim3(kThreads), 0, s, p);
+        return hipGetLastError() == hipSuccess;
+    }
     const dim3 grid((unsigned)((p.B + kWaves - 1) / kWaves));
     if (greedy) hipLaunchKernelGGL((k_small<DT, DT, true>), grid, dim3(kThreads), 0, s, p);
     else hipLaunchKernelGGL((k_small<DT, PT, false>), grid, dim3(kThreads), 0, s, p);

@@ -128,3 +128,19 @@ def test_zero_residual_fallback():
          "uniforms": synth.draw_uniforms(rng, (B, gamma + 1))}
     g, _ = _check(d)
     assert np.all(g["out_tokens"][np.arange(B), np.minimum(g["n_accepted"], gamma)] < 8)
+
+
+@pytest.mark.parametrize("V,gamma", [(16, 15), (3, 15), (16, 1), (9, 7)])
+def test_four_sequences_per_wave(V, gamma):
+    """V <= 16 and gamma < 16 run four sequences per wave (one per 16-lane
+    DPP row): a ragged batch, invalid drafts in some rows, lenience and greedy."""
+    d = synth.make_inputs("c2", 1800 + V * 16 + gamma, B=37, gamma=gamma, V=V)
+    d["draft_tokens"][5, gamma - 1] = V
+    d["draft_tokens"][18, 0] = -3
+    for lenience in (1.0, 0.4):
+        g, _ = _check(d, lenience=lenience)
+        for b in (5, 18):
+            assert g["n_accepted"][b] == -1 and np.all(g["out_tokens"][b] == -1)
+    _check(d, "greedy")
+    db = synth.make_inputs("c5", 1900 + V + gamma, B=21, gamma=gamma, V=V)
+    _check(db)
