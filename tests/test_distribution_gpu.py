@@ -16,6 +16,12 @@ Transformers via Speculative Decoding", Section 2.3 and Appendix A.1) gives:
   min(q_j, p_j) / S_j + (1 - beta_j) norm(max(0, p_j - q_j)), which is p_j
   when S_j = 1; the bonus token (n = gamma) follows p_gamma.
 
+With a lenience l in (0, 1] (same page, Appendix A.5 "Ablation Studies and
+Robustness Checks": q(x) is multiplied by l before the comparison; the draw
+after a rejection uses the residual of that same comparison, the library's
+reading where the page gives only the acceptance side) min(q_j, p_j / l)
+replaces min(q_j, p_j) and the residual is norm(max(0, p_j - l q_j)).
+
 Each case takes a different kernel path: four sequences per wave (V <= 16),
 one wave per sequence (V <= 512), and the two launches (one and several
 chunks per row).  Every tensor stays below 2 GiB.
@@ -49,7 +55,7 @@ def _softmax64(z, T):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def _run_law_case(seed, trials, gamma, V, T, ldt, pdt):
+def _run_law_case(seed, trials, gamma, V, T, ldt, pdt, lenience=1.0):
     import torch
     import exact_rejection_sampling_temp_amd as sv
 
@@ -75,16 +81,17 @@ def _run_law_case(seed, trials, gamma, V, T, ldt, pdt):
             t = t.view(torch.bfloat16)
         return t.cuda().unsqueeze(0).expand(trials, rows, V).contiguous()
 
-    print(f"[law] seed={seed} trials={trials} gamma={gamma} V={V} T={T} {ldt}/{pdt}", flush=True)
+    print(f"[law] seed={seed} trials={trials} gamma={gamma} V={V} T={T} {ldt}/{pdt} l={lenience}", flush=True)
     n, out = sv.spec_verify(dev_rows(zp_store, gamma + 1), dev_rows(q_store, gamma),
-                            torch.from_numpy(x).cuda(), torch.from_numpy(u).cuda(), T, "sample")
+                            torch.from_numpy(x).cuda(), torch.from_numpy(u).cuda(), T, "sample",
+                            lenience=lenience)
     torch.cuda.synchronize()
     n, out = n.cpu().numpy(), out.cpu().numpy()
     assert n.min() >= 0 and n.max() <= gamma
 
-    m = np.minimum(Q, P[:gamma])
+    m = np.minimum(Q, P[:gamma] / lenience)
     beta = m.sum(-1) / Q.sum(-1)
-    resid = np.maximum(0.0, P[:gamma] - Q)
+    resid = np.maximum(0.0, P[:gamma] - lenience * Q)
     resid /= resid.sum(-1, keepdims=True)
     surv = np.concatenate([[1.0], np.cumprod(beta)])
     law_n = np.append(surv[:-1] * (1 - beta), surv[-1])
@@ -114,3 +121,13 @@ def test_law_two_launches_one_chunk():
 
 def test_law_two_launches_several_chunks():
     _run_law_case(4, 4_000, 2, 40_000, 1.0, synth.BF16, synth.FP32)
+
+
+@pytest.mark.parametrize("lenience", [0.4, 0.8])
+def test_law_lenient_four_sequences_per_wave(lenience):
+    _run_law_case(5, 2_000_000, 4, 8, 1.0, synth.FP32, synth.FP32, lenience)
+
+
+@pytest.mark.parametrize("lenience", [0.4, 0.8])
+def test_law_lenient_two_launches(lenience):
+    _run_law_case(6, 60_000, 3, 3000, 0.7, synth.BF16, synth.BF16, lenience)
