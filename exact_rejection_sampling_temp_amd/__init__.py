@@ -35,7 +35,7 @@ __all__ = [
 ]
 
 EXPORTED_SYMBOLS = ("spec_verify", "spec_verify_lenient", "sv_workspace_bytes", "sv_workspace_init",
-                    "sv_status_string", "sv_standardize")
+                    "sv_status_string", "sv_standardize", "sv_extras_bytes")
 
 
 class SpecVerifyError(RuntimeError):
@@ -58,6 +58,9 @@ class Extras(ctypes.Structure):
         ("beta", ctypes.c_void_p),
         ("alpha", ctypes.c_void_p),
         ("ev_tele", ctypes.c_void_p),
+        ("error_count", ctypes.c_void_p),
+        ("withhold_partial", ctypes.c_int32),
+        ("wait_polls", ctypes.c_int32),
     ]
 
 
@@ -80,6 +83,11 @@ def load_library(path: str = LIB_PATH):
             raise ImportError(
                 f"{path} is missing: build it first (python -m exact_rejection_sampling_temp_amd.build)")
         lib = ctypes.CDLL(path)
+        lib.sv_extras_bytes.restype = ctypes.c_size_t
+        lib.sv_extras_bytes.argtypes = []
+        if lib.sv_extras_bytes() != ctypes.sizeof(Extras):
+            raise ImportError(f"{path}: sv_extras_t is {lib.sv_extras_bytes()} bytes, the binding's mirror "
+                              f"{ctypes.sizeof(Extras)}: rebuild the library or update Extras")
         lib.sv_workspace_bytes.restype = ctypes.c_size_t
         lib.sv_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.sv_workspace_init.restype = ctypes.c_int
@@ -128,17 +136,21 @@ def sv_workspace_init(workspace, stream=None) -> None:
         raise SpecVerifyError(rc, "sv_workspace_init")
 
 
-# One zero-initialised workspace per device, grown on demand.  Calls that
-# overlap on one device (different streams, no ordering) must pass their own.
+# One zero-initialised workspace per (device, stream), grown on demand.  It
+# is allocated and zero-filled on the stream that uses it, so the fill is
+# ordered before that stream's kernels, a replaced (smaller) one is freed
+# through the caching allocator on the same stream, and calls on different
+# streams never share one.
 _ws_cache: dict = {}
 
 
-def _workspace(device, nbytes: int):
+def _workspace(device, nbytes: int, stream):
     import torch
-    key = (device.type, device.index)
+    key = (device.type, device.index, int(stream.cuda_stream))
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 
@@ -164,7 +176,8 @@ def _dtype_tag(t) -> int:
 
 def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature: float = 1.0,
                 mode: str | int = "sample", *, n_accepted=None, out_tokens=None, workspace=None,
-                aux: dict | None = None, events=None, stream=None, lenience: float = 1.0):
+                aux: dict | None = None, events=None, stream=None, lenience: float = 1.0,
+                error_count=None, _test_withhold_partial: int = 0, _test_wait_polls: int = 0):
     """Batched verify-and-sample on the GPU.
 
     target_logits [B, gamma+1, V] fp32/bf16, draft_probs [B, gamma, V] fp32/bf16
@@ -180,6 +193,10 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     ``events``: optional (begin, mid, end) or (begin, mid, end, tele) raw
     hipEvent_t handles (ints); tele is recorded after the telemetry sweep.
     ``lenience``: l in [0, 1] (spec_verify_lenient); 1 calls spec_verify.
+    ``error_count``: optional uint32 device counter (one element, zeroed by
+    the caller) of sequences whose outputs were withheld because a bounded
+    device-side wait ran out (n_accepted = -2).  ``_test_withhold_partial``,
+    ``_test_wait_polls``: sv_extras_t's test hooks for that failure path.
     """
     import torch
     lib = load_library()
@@ -219,12 +236,18 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
         dt, per = _AUX_SPEC[k]
         _check_out(t, getattr(torch, dt), {"B": B, "G": gamma, "BG": B * gamma, "BG1": B * G1}[per], dev, k)
     need = lib.sv_workspace_bytes(B, gamma, V)
-    if workspace is None:
-        workspace = _workspace(dev, need)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if workspace is None:
+        workspace = _workspace(dev, need, s)
     ex = None
-    if aux or events:
+    if error_count is not None:
+        _check_out(error_count, torch.int32, 1, dev, "error_count")
+    if aux or events or error_count is not None or _test_withhold_partial or _test_wait_polls:
         ex = Extras()
+        if error_count is not None:
+            ex.error_count = error_count.data_ptr()
+        ex.withhold_partial = int(_test_withhold_partial)
+        ex.wait_polls = int(_test_wait_polls)
         for k, t in (aux or {}).items():
             setattr(ex, k, t.data_ptr())
         if events:

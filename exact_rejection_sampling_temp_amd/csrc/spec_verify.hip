@@ -67,6 +67,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr uint64_t kInvalidBit = 1ull << 63;
+// SeqCtl::pad[0], bit k: the merge of row k ran out of its bounded wait for a
+// partial (the sequence's outputs are withheld if k is on its walk, k <= n)
 constexpr double kResidEps = 1e-15;  // [ST] correction_distribution
 constexpr double kLog2e = 1.4426950408889634073599246810018921;
 
@@ -644,6 +646,10 @@ struct Params {
     double cd;         // log2(e)/T in double
     double len;        // lenience l in [0, 1] (1: the exact method)
     Exp2Coef ex;       // kExp2Coef
+    int polls_slot;    // bound of a merge's wait for a partial slot
+    int drop_slot;     // test hook: >= 0 makes chunk 0 of that position withhold its
+                       // partial, so that the merge's bounded wait runs out
+    uint32_t* err_count;  // optional: sequences whose merge wait ran out
 };
 
 // bits 0 .. gamma (one per row of a sequence)
@@ -671,7 +677,7 @@ constexpr int kCountBits = 16;
 // merge of a row's partials: slots per lane per pass, and the bound of the
 // wait for a slot whose store is still in flight
 constexpr int kMaxSlotsPerLane = 1;
-constexpr int kSlotPolls = 1 << 20;
+constexpr int kSlotPolls = 1 << 20;  // default bound of a merge's wait for a partial (~28 ms)
 constexpr uint64_t kSlotFlag = 1ull << 32;  // above the max's float bits in a partial's first word
 constexpr uint64_t kSignBit = 1ull << 63;
 constexpr uint64_t kCountMask = (1ull << kCountBits) - 1ull;
@@ -900,8 +906,11 @@ __device__ void finish_wave(const Params& p, int b)
     load_round(0);
 
     const bool bad = __ballot(lane < p.gamma && (tok < 0 || tok >= p.V)) != 0;
-    const bool invalid = (mask & kInvalidBit) || bad;
     const int n = first_reject(mask, p.gamma);
+    // a row on the walk whose merge ran out of its wait: the sequence is
+    // reported like an invalid one, with n = -2, and counted
+    const bool failed = (ld_agent(&p.ctl[b].pad[0]) & ((2ull << n) - 1ull)) != 0;
+    const bool invalid = (mask & kInvalidBit) || bad || failed;
     const bool resid = n < p.gamma;
     int t = -1;
     double Z = NAN;
@@ -933,7 +942,9 @@ __device__ void finish_wave(const Params& p, int b)
         // totals scanned across the wave, then the crossing lane's entries
         int js = -1;
         double carry = 0.0, pre = 0.0;
-        for (int r = 0; r < nrounds && js < 0; ++r) {
+        // u >= 1 puts u * total at the end of the row: no running sum exceeds
+        // it, and the draw is the largest index with positive weight (below)
+        for (int r = 0; r < nrounds && js < 0 && ug < 1.0; ++r) {
             if (nrounds > 1) load_round(r);
             double lt = 0.0;
 #pragma unroll
@@ -1059,7 +1070,8 @@ __device__ void finish_wave(const Params& p, int b)
         }
     }
     if (lane == 0) {
-        p.n_out[b] = invalid ? -1 : n;
+        if (failed && p.err_count) add_agent(p.err_count, 1u);
+        p.n_out[b] = failed ? -2 : invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = (!invalid && resid) ? Z : NAN;
     }
 }
@@ -1163,7 +1175,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
             const uint64_t m = ld_agent(&p.ctl[b].mask);
             const uint64_t d = ld_agent(&p.ctl[b].dec);
             const uint64_t cl0 = ld_agent(&p.ctl[b].claim);
-            if ((m & kInvalidBit) || (m & ((1ull << k) - 1ull))) {
+            // Only a reject bit below k makes row k unneeded.  A bad draft
+            // token at position j sets kInvalidBit together with reject bit
+            // j, so rows past j skip while every row before j is still
+            // streamed and decided: each position of the sequence then gets
+            // a decision bit, and its last user clears the workspace.
+            if (m & ((1ull << k) - 1ull)) {
                 cmd = -1;
                 const uint64_t all = rows_mask(p.gamma);
                 if (k >= kHelpFrom && (d & all) == all && (uint32_t)cl0 < (uint32_t)p.nch2) {
@@ -1247,8 +1264,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
             // the sum, never negative, goes out with its sign bit flipped;
             // the two stores may land in either order)
             uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + c);
-            st_agent(slot, (uint64_t)__float_as_uint(mx) | kSlotFlag);
-            st_agent(slot + 1, dbits(s) ^ kSignBit);
+            if (!(k == p.drop_slot && c == 0)) {
+                st_agent(slot, (uint64_t)__float_as_uint(mx) | kSlotFlag);
+                st_agent(slot + 1, dbits(s) ^ kSignBit);
+            }
             if (k < p.gamma && xk >= 0 && xk < p.V) {
                 evidence = rejection_evidence((double)uk, p.len * (double)word_elem<PT>(qw, qsel), s, mx,
                                               word_elem<DT>(zw, zsel), p.cd, p.ex);
@@ -1266,6 +1285,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
     double S = 0.0;
     float mj[kMaxSlotsPerLane];
     double sj[kMaxSlotsPerLane];
+    bool lost = false;  // a slot that did not land within the bounded wait
     for (int j0 = 0; j0 < p.nch1; j0 += 64 * kMaxSlotsPerLane) {
 #pragma unroll
         for (int r = 0; r < kMaxSlotsPerLane; ++r) {
@@ -1275,14 +1295,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
                 const uint64_t* slot = p.part1 + 2 * ((size_t)row * p.nch1 + j);
                 w0 = ld_agent(slot);
                 w1 = ld_agent(slot + 1);
-                for (int it = 0; (w0 == 0 || w1 == 0) && it < kSlotPolls; ++it) {
+                for (int it = 0; (w0 == 0 || w1 == 0) && it < p.polls_slot; ++it) {
                     __builtin_amdgcn_s_sleep(1);
                     w0 = ld_agent(slot);
                     w1 = ld_agent(slot + 1);
                 }
+                if (w0 == 0 || w1 == 0) {
+                    lost = true;
+                    w0 = w1 = 0;
+                }
             }
-            mj[r] = j < p.nch1 ? __uint_as_float((uint32_t)w0) : -INFINITY;
-            sj[r] = __longlong_as_double((long long)(w1 ^ kSignBit));
+            mj[r] = j < p.nch1 && w0 != 0 ? __uint_as_float((uint32_t)w0) : -INFINITY;
+            sj[r] = w1 != 0 ? __longlong_as_double((long long)(w1 ^ kSignBit)) : 0.0;
         }
         float mm = -INFINITY;
 #pragma unroll
@@ -1298,6 +1322,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
             if (mj[r] > -INFINITY) S += sj[r] * exp2_f64(((double)mj[r] - (double)M) * p.cd, p.ex);
     }
     S = wave_sum(S);
+    const bool failed = __ballot(lost) != 0;
 
     if (threadIdx.x == 0) {
         double P = NAN, Q = NAN;
@@ -1315,10 +1340,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
                 if (!((double)uk <= thr)) maskbits = 1ull << k;
             }
         }
+        // the failure mark (its sequence's outputs are withheld), the
         // statistics, then the reject bit, then the decision bit that
-        // announces both (a rejection decides every later position too)
+        // announces them (a rejection decides every later position too)
+        uint64_t dd = 0;
+        if (failed) dd ^= or_agent(&p.ctl[b].pad[0], 1ull << k);
         const uint64_t w[4] = {stat_word0(M, -1), dbits(S), dbits(P), dbits(Q)};
-        uint64_t dd = publish(reinterpret_cast<uint64_t*>(p.stats + row), w, p.zero);
+        dd ^= publish(reinterpret_cast<uint64_t*>(p.stats + row), w, p.zero);
         if (maskbits) dd ^= or_agent(&p.ctl[b].mask, maskbits) & p.zero;
         const uint64_t all = rows_mask(p.gamma);
         const uint64_t decbits = maskbits ? (all & ~((1ull << k) - 1ull)) : (1ull << k);
@@ -1472,8 +1500,9 @@ __device__ __forceinline__ bool greedy_skipped(const Params& p, int b, int k, in
 {
     if (k == 0) return false;  // position 0 is always needed (k is uniform)
     if (threadIdx.x == 0) {
+        // (a bad token at position j also sets reject bit j: see k_main_sample)
         const uint64_t m = ld_agent(&p.ctl[b].mask);
-        *sm_flag = ((m & kInvalidBit) | (m & ((1ull << k) - 1ull))) ? 1 : 0;
+        *sm_flag = (m & ((1ull << k) - 1ull)) ? 1 : 0;
     }
     __syncthreads();
     return *sm_flag != 0;
@@ -2030,6 +2059,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 extern "C" {
 
+size_t sv_extras_bytes(void) { return sizeof(sv_extras_t); }
+
 size_t sv_workspace_bytes(int batch, int gamma, int vocab)
 {
     if (batch < 1 || gamma < 1 || gamma > SV_MAX_GAMMA || vocab < 1) return 0;
@@ -2159,6 +2190,9 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     p.cd = cd;
     p.ex = kExp2Coef;
     p.len = greedy ? 1.0 : (double)lenience;
+    p.polls_slot = extras && extras->wait_polls > 0 ? extras->wait_polls : kSlotPolls;
+    p.drop_slot = extras && extras->withhold_partial > 0 ? extras->withhold_partial - 1 : -1;
+    p.err_count = extras ? extras->error_count : nullptr;
 
     hipEvent_t ev_mid = extras ? (hipEvent_t)extras->ev_mid : nullptr;
     if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)

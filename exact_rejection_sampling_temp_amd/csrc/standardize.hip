@@ -718,7 +718,6 @@ __global__ __launch_bounds__(kHThreads) void k_standardize_b16(const StdParams s
             const uint32_t w = word_of(cw[wi >> 2], wi & 3);
             return (j & 1) ? (w & 0xffffu) : (w >> 16);
         };
-        const uint32_t key_hi = 65535u - 64u * (uint32_t)tid;
         uint32_t c_loc = 0;
 #pragma unroll
         for (int j = 65536 / kHThreads - 1; j >= 0; --j) c_loc += cnt_at(j);  // 64 keys per thread

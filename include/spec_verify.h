@@ -110,7 +110,24 @@ typedef struct {
     /* hipEvent_t recorded after the telemetry sweep (before the last launch)
      * when the sweep runs; may be NULL. */
     void* ev_tele;
+    /* Device counter (may be NULL): incremented once for every sequence
+     * whose outputs were withheld because a bounded device-side wait for
+     * another workgroup's partial result ran out (n_accepted[b] = -2, every
+     * token -1; see spec_verify).  The caller zeroes it. */
+    uint32_t* error_count;
+    /* Tests of that failure path only; leave both 0.  withhold_partial =
+     * k + 1 makes the workgroup of the first chunk of every row at position
+     * k withhold its partial row statistics (sample mode, vocab > 512), and
+     * wait_polls > 0 bounds the merge's wait for a partial to that many
+     * polls, so that the wait runs out and the sequences are reported as
+     * failed while every kernel still completes normally. */
+    int32_t withhold_partial;
+    int32_t wait_polls;
 } sv_extras_t;
+
+/* sizeof(sv_extras_t) as this library was built: a binding that mirrors
+ * the struct checks its own size against it before passing one. */
+size_t sv_extras_bytes(void);
 
 /* Workspace size in bytes for a problem shape (any mode). */
 size_t sv_workspace_bytes(int batch, int gamma, int vocab);
@@ -137,7 +154,13 @@ int sv_workspace_init(void* workspace, size_t bytes, void* stream);
  *                         greedy mode
  *   temperature           T > 0, finite, in sample mode; ignored in greedy mode
  *   mode                  SV_SAMPLE or SV_GREEDY
- *   n_accepted            [B] int32 out: accepted drafts n in [0, gamma], or -1
+ *   n_accepted            [B] int32 out: accepted drafts n in [0, gamma]; -1 for
+ *                         an invalid draft token; -2 if a bounded device-side
+ *                         wait for another workgroup's partial row statistics
+ *                         ran out (never expected: the wait covers stores that
+ *                         were issued before the count that started it; the
+ *                         sequence's tokens are then all -1 and
+ *                         extras->error_count, if given, counts it)
  *   out_tokens            [B][gamma+1] int32 out: x_0..x_{n-1}, t, then -1
  *   workspace             device buffer of >= sv_workspace_bytes(B, gamma, V)
  *                         bytes, 256-byte aligned, zero-filled before first use

@@ -71,13 +71,33 @@ def run_ref(d: dict, mode: str = "sample", telemetry: bool = False, lenience: fl
                                   lenience=lenience)
 
 
-def compare(gpu: dict, ref: dict, gamma: int) -> dict:
+def well_formed(n, out, draft_tokens, vocab: int, gamma: int):
+    """Indices of sequences whose outputs break the block-advance rule: a
+    valid sequence has 0 <= n <= gamma, out[:n] == its drafts, out[n] a token
+    in [0, vocab) and -1 after it; an invalid one (n = -1) is all -1."""
+    pos = np.arange(gamma + 1)[None, :]
+    nn = n[:, None]
+    inval = n == -1
+    ok_n = (n >= -1) & (n <= gamma)
+    prefix = np.where(pos < nn, out == np.pad(draft_tokens, ((0, 0), (0, 1)), constant_values=-2), True)
+    at_n = np.where(pos == nn, (out >= 0) & (out < vocab), True)
+    after = np.where(pos > nn, out == -1, True)
+    valid_ok = prefix.all(1) & at_n.all(1) & after.all(1)
+    inval_ok = np.all(out == -1, axis=1)
+    good = ok_n & np.where(inval, inval_ok, valid_ok)
+    return np.nonzero(~good)[0]
+
+
+def compare(gpu: dict, ref: dict, gamma: int, draft_tokens=None, vocab: int | None = None) -> dict:
     """Bit-exact agreement except downstream of a near-boundary decision.
 
     A sequence whose oracle walk has no flagged decision must match exactly.
-    For a sequence whose first flagged decision is at position f, only the
-    outputs before f are required to match (every later output depends on
-    the flagged decision).  Returns counts for reporting."""
+    For a sequence whose first flagged decision is at position f, the
+    outputs before f must match and n must be at least f (every later output
+    depends on the flagged decision); given the draft tokens and the
+    vocabulary size, every sequence's outputs must also be well formed
+    (well_formed), the flagged ones included.  Returns counts for
+    reporting."""
     n_g, o_g = gpu["n_accepted"], gpu["out_tokens"]
     n_r, o_r = ref["n_accepted"], ref["out_tokens"]
     fp = ref["flag_pos"]
@@ -91,8 +111,16 @@ def compare(gpu: dict, ref: dict, gamma: int) -> dict:
     flagged = np.nonzero(~clean)[0]
     for b in flagged:
         f = fp[b]
-        assert n_g[b] >= f, (b, f, n_g[b])
+        assert n_r[b] >= 0 and f <= n_r[b], (b, f, n_r[b])
+        assert f <= n_g[b] <= gamma, (b, f, n_g[b])
         assert np.array_equal(o_g[b, :f], o_r[b, :f]), b
+    if draft_tokens is not None:
+        assert vocab is not None
+        wf = well_formed(np.asarray(n_g), np.asarray(o_g), np.asarray(draft_tokens), vocab, gamma)
+        if wf.size:
+            b = wf[0]
+            raise AssertionError(f"{wf.size} sequences with malformed outputs; first b={b}: n={n_g[b]} "
+                                 f"out={o_g[b].tolist()} drafts={np.asarray(draft_tokens)[b].tolist()}")
     return {"sequences": int(n_r.size), "flagged_sequences": int(flagged.size),
             "decisions": int(ref["n_decisions"].sum()), "flagged_decisions": int(ref["n_flags"].sum())}
 

@@ -37,6 +37,18 @@ def test_library_loads_and_exports_declared_symbols():
         assert hasattr(lib, name), name
 
 
+def test_extras_mirror_matches_the_library():
+    # the binding's ctypes copy of sv_extras_t must be exactly the struct the
+    # library reads: a shorter mirror leaves the library reading host memory
+    # past its end (uninitialised fields, device pointers among them)
+    lib = sv.load_library()
+    assert lib.sv_extras_bytes() == ctypes.sizeof(sv.Extras)
+    fields = re.search(r"typedef struct \{(.*?)\} sv_extras_t;", _header_text(), flags=re.S).group(1)
+    fields = re.sub(r"/\*.*?\*/", "", fields, flags=re.S)
+    names = re.findall(r"([A-Za-z_]\w*)\s*;", fields)
+    assert names == [f[0] for f in sv.Extras._fields_]
+
+
 def test_binding_constants_match_header():
     d = _header_defines()
     for k in ("SV_FP32", "SV_BF16", "SV_SAMPLE", "SV_GREEDY", "SV_MAX_GAMMA", "SV_OK"):

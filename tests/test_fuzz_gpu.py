@@ -32,6 +32,6 @@ def test_random_shapes(case):
     else:
         r = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"], d["uniforms"],
                                    d["temperature"], oracle.SAMPLE, lenience=lenience)
-    compare(g, r, gamma)
+    compare(g, r, gamma, draft_tokens=d["draft_tokens"], vocab=d["V"])
     if mode == "sample":
         check_aux(g, r, 1e-6)

@@ -18,7 +18,7 @@ def _check_len(d, l):
     print(f"[lenience] {d['name']} B={d['B']} gamma={d['gamma']} V={d['V']} l={l}", flush=True)
     g = run_gpu(d, lenience=l)
     r = run_ref(d, lenience=l)
-    c = compare(g, r, d["gamma"])
+    c = compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
     check_aux(g, r, 1e-6)
     assert c["flagged_decisions"] <= max(1, c["decisions"] // 1000)
     return g, r
@@ -57,4 +57,4 @@ def test_lenient_scalar_path_and_repeated_calls():
     d = synth.make_inputs("c2", 80, B=6, V=4000)
     g = run_gpu(d)
     r = run_ref(d)
-    compare(g, r, d["gamma"])
+    compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])

@@ -25,7 +25,7 @@ def _check(d, mode="sample", aux=True):
     print(f"[parity] {d['name']} B={d['B']} gamma={d['gamma']} V={d['V']} mode={mode}", flush=True)
     g = run_gpu(d, mode, with_aux=aux and mode == "sample")
     r = run_ref(d, mode)
-    c = compare(g, r, d["gamma"])
+    c = compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
     for k in _STATS:
         _STATS[k] += c[k]
     if aux and mode == "sample":

@@ -22,7 +22,7 @@ def _check(d, mode="sample", lenience=1.0):
         import oracle
         r = oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"], d["uniforms"],
                                    d["temperature"], oracle.SAMPLE, lenience=lenience)
-    compare(g, r, d["gamma"])
+    compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
     if mode == "sample":
         check_aux(g, r, 1e-6)
     return g, r

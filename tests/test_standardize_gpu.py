@@ -107,7 +107,7 @@ def test_verify_on_standardised_rows(k):
     ds["target_logits"] = zs
     g = run_gpu(ds)
     r = run_ref(ds)
-    compare(g, r, d["gamma"])
+    compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
     # every emitted token is inside its row's top-k
     for b in range(B):
         n = r["n_accepted"][b]

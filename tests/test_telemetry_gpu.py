@@ -24,7 +24,7 @@ def _check_tele(d, with_aux=True):
     print(f"[telemetry] {d['name']} B={d['B']} gamma={d['gamma']} V={d['V']}", flush=True)
     g = run_gpu(d, with_aux=with_aux, telemetry=True)
     r = run_ref(d, telemetry=True)
-    compare(g, r, d["gamma"])
+    compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
     if with_aux:
         check_aux(g, r, 1e-6)
     assert np.all(np.isfinite(g["beta"])) and np.all(np.isfinite(g["alpha"]))
