@@ -29,13 +29,13 @@ SV_TOPK = 0
 SV_TOPP = 1
 
 __all__ = [
-    "spec_verify", "standardize", "sv_workspace_bytes", "sv_workspace_init", "sv_status_string",
+    "spec_verify", "spec_verify_noalloc", "standardize", "sv_workspace_bytes", "sv_workspace_init", "sv_status_string",
     "SpecVerifyError", "load_library", "EXPORTED_SYMBOLS",
     "SV_FP32", "SV_BF16", "SV_SAMPLE", "SV_GREEDY", "SV_MAX_GAMMA",
 ]
 
-EXPORTED_SYMBOLS = ("spec_verify", "spec_verify_lenient", "sv_workspace_bytes", "sv_workspace_init",
-                    "sv_status_string", "sv_standardize", "sv_extras_bytes")
+EXPORTED_SYMBOLS = ("spec_verify", "spec_verify_lenient", "spec_verify_noalloc", "sv_workspace_bytes",
+                    "sv_workspace_init", "sv_status_string", "sv_standardize", "sv_extras_bytes")
 
 
 class SpecVerifyError(RuntimeError):
@@ -114,6 +114,14 @@ def load_library(path: str = LIB_PATH):
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
             ctypes.POINTER(Extras), ctypes.c_void_p,
         ]
+        lib.spec_verify_noalloc.restype = ctypes.c_int
+        lib.spec_verify_noalloc.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_float, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.POINTER(Extras), ctypes.c_void_p,
+        ]
         _lib = lib
         return lib
 
@@ -177,7 +185,8 @@ def _dtype_tag(t) -> int:
 def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature: float = 1.0,
                 mode: str | int = "sample", *, n_accepted=None, out_tokens=None, workspace=None,
                 aux: dict | None = None, events=None, stream=None, lenience: float = 1.0,
-                error_count=None, _test_withhold_partial: int = 0, _test_wait_polls: int = 0):
+                error_count=None, _test_withhold_partial: int = 0, _test_wait_polls: int = 0,
+                _noalloc: bool = False):
     """Batched verify-and-sample on the GPU.
 
     target_logits [B, gamma+1, V] fp32/bf16, draft_probs [B, gamma, V] fp32/bf16
@@ -235,10 +244,9 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
             raise ValueError(f"unknown aux output {k!r}")
         dt, per = _AUX_SPEC[k]
         _check_out(t, getattr(torch, dt), {"B": B, "G": gamma, "BG": B * gamma, "BG1": B * G1}[per], dev, k)
-    need = lib.sv_workspace_bytes(B, gamma, V)
     s = stream if stream is not None else torch.cuda.current_stream(dev)
-    if workspace is None:
-        workspace = _workspace(dev, need, s)
+    if workspace is None and not _noalloc:
+        workspace = _workspace(dev, lib.sv_workspace_bytes(B, gamma, V), s)
     ex = None
     if error_count is not None:
         _check_out(error_count, torch.int32, 1, dev, "error_count")
@@ -260,6 +268,12 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
             _dtype_tag(draft_probs) if m == SV_SAMPLE else 0,
             draft_tokens.data_ptr(), uniforms.data_ptr() if m == SV_SAMPLE else None,
             float(temperature))
+    if _noalloc:
+        rc = lib.spec_verify_noalloc(*head, float(lenience), m, n_accepted.data_ptr(), out_tokens.data_ptr(),
+                                     ctypes.byref(ex) if ex is not None else None, s.cuda_stream)
+        if rc != SV_OK:
+            raise SpecVerifyError(rc, "spec_verify_noalloc")
+        return n_accepted, out_tokens
     tail = (m, n_accepted.data_ptr(), out_tokens.data_ptr(),
             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
             ctypes.byref(ex) if ex is not None else None,
@@ -271,6 +285,19 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     if rc != SV_OK:
         raise SpecVerifyError(rc)
     return n_accepted, out_tokens
+
+
+def spec_verify_noalloc(target_logits, draft_probs, draft_tokens, uniforms, temperature: float = 1.0,
+                        mode: str | int = "sample", *, n_accepted=None, out_tokens=None, aux: dict | None = None,
+                        events=None, stream=None, lenience: float = 1.0, error_count=None):
+    """spec_verify through the allocation-free entry point spec_verify_noalloc
+    (its workspace is the library's static per-GPU scratch array; calls that
+    overlap on one GPU race).  For callers that cannot allocate, pass
+    preallocated ``n_accepted`` and ``out_tokens``: then nothing is allocated
+    on any path of the call.  Arguments and results as for spec_verify."""
+    return spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature, mode,
+                       n_accepted=n_accepted, out_tokens=out_tokens, aux=aux, events=events, stream=stream,
+                       lenience=lenience, error_count=error_count, _noalloc=True)
 
 
 def standardize(logits, method: str | int, k: int = 0, top_p: float = 1.0, temperature: float = 1.0, *,

@@ -59,6 +59,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "spec_verify.h"
 
@@ -2055,6 +2056,68 @@ bool launch_greedy_t(bool vec, int grid1, int B, const Params& p, hipStream_t s,
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The checks of every verify entry point that need no workspace and no HIP
+// call; SV_OK or the status to return.
+int check_args(int batch, int gamma, int vocab, const void* target_logits, int logits_dtype,
+               const void* draft_probs, int probs_dtype, const int32_t* draft_tokens, const float* uniforms,
+               float temperature, float lenience, int mode, const int32_t* n_accepted, const int32_t* out_tokens)
+{
+    if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_ERR_MODE;
+    if (batch < 1) return SV_ERR_BATCH;
+    if (gamma < 1 || gamma > SV_MAX_GAMMA) return SV_ERR_GAMMA;
+    if (vocab < 1) return SV_ERR_VOCAB;
+    if (logits_dtype != SV_FP32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+    const bool greedy = mode == SV_GREEDY;
+    if (!target_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_ERR_NULL_POINTER;
+    if (!greedy) {
+        if (!draft_probs || !uniforms) return SV_ERR_NULL_POINTER;
+        if (probs_dtype != SV_FP32 && probs_dtype != SV_BF16) return SV_ERR_DTYPE;
+        if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SV_ERR_TEMPERATURE;
+        if (!(lenience >= 0.0f && lenience <= 1.0f)) return SV_ERR_LENIENCE;
+    }
+    const size_t lsz = logits_dtype == SV_BF16 ? 2 : 4;
+    const size_t psz = probs_dtype == SV_BF16 ? 2 : 4;
+    if (!aligned(target_logits, lsz) || !aligned(draft_tokens, 4) || !aligned(n_accepted, 4) ||
+        !aligned(out_tokens, 4))
+        return SV_ERR_ALIGNMENT;
+    if (!greedy && (!aligned(draft_probs, psz) || !aligned(uniforms, 4))) return SV_ERR_ALIGNMENT;
+    return SV_OK;
+}
+
+}  // namespace
+
+// The workspace of spec_verify_noalloc: one file-scope device array per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// the array's name to a kernel or a copy (on the host it is only a
+// stand-in): it uses the device address that hipGetSymbolAddress returns,
+// fetched once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, fetched and zero-filled (with a
+// kernel, on `s`) on the first call on that device; nullptr on failure.
+void* scratch_for_current_device(hipStream_t s)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    // (a workspace must be zero before its first use)
+    constexpr size_t n16 = SV_NOALLOC_SCRATCH_BYTES / 16;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint4*>(ptr), n16, static_cast<unsigned char*>(ptr), (size_t)0);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2106,25 +2169,11 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
                         const sv_extras_t* extras, void* stream)
 {
     // ---- argument validation (no HIP call before this block passes)
-    if (mode != SV_SAMPLE && mode != SV_GREEDY) return SV_ERR_MODE;
-    if (batch < 1) return SV_ERR_BATCH;
-    if (gamma < 1 || gamma > SV_MAX_GAMMA) return SV_ERR_GAMMA;
-    if (vocab < 1) return SV_ERR_VOCAB;
-    if (logits_dtype != SV_FP32 && logits_dtype != SV_BF16) return SV_ERR_DTYPE;
+    const int bad = check_args(batch, gamma, vocab, target_logits, logits_dtype, draft_probs, probs_dtype,
+                               draft_tokens, uniforms, temperature, lenience, mode, n_accepted, out_tokens);
+    if (bad != SV_OK) return bad;
     const bool greedy = mode == SV_GREEDY;
-    if (!target_logits || !draft_tokens || !n_accepted || !out_tokens) return SV_ERR_NULL_POINTER;
-    if (!greedy) {
-        if (!draft_probs || !uniforms) return SV_ERR_NULL_POINTER;
-        if (probs_dtype != SV_FP32 && probs_dtype != SV_BF16) return SV_ERR_DTYPE;
-        if (!(temperature > 0.0f) || !std::isfinite(temperature)) return SV_ERR_TEMPERATURE;
-        if (!(lenience >= 0.0f && lenience <= 1.0f)) return SV_ERR_LENIENCE;
-    }
     const size_t lsz = logits_dtype == SV_BF16 ? 2 : 4;
-    const size_t psz = probs_dtype == SV_BF16 ? 2 : 4;
-    if (!aligned(target_logits, lsz) || !aligned(draft_tokens, 4) || !aligned(n_accepted, 4) ||
-        !aligned(out_tokens, 4))
-        return SV_ERR_ALIGNMENT;
-    if (!greedy && (!aligned(draft_probs, psz) || !aligned(uniforms, 4))) return SV_ERR_ALIGNMENT;
     const Layout L = make_layout(batch, gamma, vocab);
     if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SV_ERR_ALIGNMENT;
@@ -2215,6 +2264,25 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     return SV_OK;
 }
 
+int spec_verify_noalloc(int batch, int gamma, int vocab,
+                        const void* target_logits, int logits_dtype,
+                        const void* draft_probs, int probs_dtype,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        float temperature, float lenience, int mode,
+                        int32_t* n_accepted, int32_t* out_tokens,
+                        const sv_extras_t* extras, void* stream)
+{
+    const int bad = check_args(batch, gamma, vocab, target_logits, logits_dtype, draft_probs, probs_dtype,
+                               draft_tokens, uniforms, temperature, lenience, mode, n_accepted, out_tokens);
+    if (bad != SV_OK) return bad;
+    if (sv_workspace_bytes(batch, gamma, vocab) > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+    void* ws = scratch_for_current_device((hipStream_t)stream);
+    if (!ws) return SV_ERR_LAUNCH;
+    return spec_verify_lenient(batch, gamma, vocab, target_logits, logits_dtype, draft_probs, probs_dtype,
+                               draft_tokens, uniforms, temperature, lenience, mode, n_accepted, out_tokens,
+                               ws, SV_NOALLOC_SCRATCH_BYTES, extras, stream);
+}
+
 const char* sv_status_string(int status)
 {
     switch (status) {
@@ -2232,6 +2300,7 @@ const char* sv_status_string(int status)
     case SV_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case SV_ERR_LENIENCE: return "lenience must be in [0, 1] in sample mode";
     case SV_ERR_STANDARDIZE: return "standardisation needs SV_TOPK with k >= 1 or SV_TOPP with 0 < top_p <= 1";
+    case SV_ERR_SCRATCH: return "spec_verify_noalloc: the problem needs more workspace than its static scratch array (SV_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

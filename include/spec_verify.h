@@ -69,6 +69,11 @@ extern "C" {
 #define SV_ERR_LAUNCH -11       /* the HIP runtime rejected a kernel launch          */
 #define SV_ERR_LENIENCE -12     /* sample mode with lenience outside [0, 1]          */
 #define SV_ERR_STANDARDIZE -13  /* unknown method, k < 1, or top_p outside (0, 1]    */
+#define SV_ERR_SCRATCH -14      /* spec_verify_noalloc: sv_workspace_bytes() of the
+                                   shape exceeds SV_NOALLOC_SCRATCH_BYTES            */
+
+/* Size of the static per-GPU scratch array of spec_verify_noalloc. */
+#define SV_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 /* Standardisation methods (sv_standardize). */
 #define SV_TOPK 0
@@ -205,6 +210,31 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
                         float temperature, float lenience, int mode,
                         int32_t* n_accepted, int32_t* out_tokens,
                         void* workspace, size_t workspace_bytes,
+                        const sv_extras_t* extras, void* stream);
+
+/*
+ * spec_verify_noalloc -- spec_verify_lenient without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * allocates nothing: its workspace is a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES (8 MiB) in the library, one per GPU, held until
+ * the process ends.  The first call on a device looks up the array's
+ * address and zero-fills it with a kernel on `stream`; every completed call
+ * leaves it zero again.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on the same GPU (other streams, other threads) race,
+ * and after SV_ERR_LAUNCH the array must be considered dirty (later calls
+ * may give wrong results).  Returns SV_ERR_SCRATCH, without launching
+ * anything, when sv_workspace_bytes(batch, gamma, vocab) exceeds the array
+ * (batch up to 594 at gamma 8 and vocab 152 064 fits, and up to 280 at
+ * gamma 16 and vocab 256 000).  Every other argument, the results and the status codes as for
+ * spec_verify_lenient.
+ */
+int spec_verify_noalloc(int batch, int gamma, int vocab,
+                        const void* target_logits, int logits_dtype,
+                        const void* draft_probs, int probs_dtype,
+                        const int32_t* draft_tokens, const float* uniforms,
+                        float temperature, float lenience, int mode,
+                        int32_t* n_accepted, int32_t* out_tokens,
                         const sv_extras_t* extras, void* stream);
 
 /*

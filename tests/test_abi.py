@@ -136,6 +136,34 @@ def test_lenient_entry_point_validation():
     assert call(0.5, T=0.0) == d["SV_ERR_TEMPERATURE"]
 
 
+def test_noalloc_entry_point_validation():
+    """The allocation-free entry point checks its arguments, then that the
+    workspace fits its static scratch array, before any HIP call."""
+    d = _header_defines()
+    lib = sv.load_library()
+
+    def call(B=2, gamma=3, V=100, mode=sv.SV_SAMPLE, T=1.0, l=1.0, logits=FAKE):
+        return lib.spec_verify_noalloc(B, gamma, V, logits, sv.SV_BF16, FAKE, sv.SV_FP32, FAKE, FAKE, T, l, mode,
+                                       FAKE, FAKE, None, None)
+    assert call(mode=7) == d["SV_ERR_MODE"]
+    assert call(B=0) == d["SV_ERR_BATCH"]
+    assert call(gamma=sv.SV_MAX_GAMMA + 1) == d["SV_ERR_GAMMA"]
+    assert call(T=0.0) == d["SV_ERR_TEMPERATURE"]
+    assert call(l=1.5) == d["SV_ERR_LENIENCE"]
+    assert call(logits=None) == d["SV_ERR_NULL_POINTER"]
+    assert call(logits=FAKE + 1) == d["SV_ERR_ALIGNMENT"]
+    # 1024 x 9 rows of 152064 need about 13.8 MiB of workspace: more than the 8 MiB array
+    m = re.search(r"#define\s+SV_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", _header_text())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == 8 << 20
+    assert sv.sv_workspace_bytes(1024, 8, 152_064) > limit
+    assert call(B=1024, gamma=8, V=152_064) == d["SV_ERR_SCRATCH"]
+    assert call(B=1024, gamma=8, V=152_064, mode=sv.SV_GREEDY) == d["SV_ERR_SCRATCH"]
+    # every shape the benchmark and the tests use fits
+    for B, g, V in ((1, 4, 8), (8, 4, 32_000), (64, 4, 128_256), (256, 8, 152_064), (32, 16, 256_000)):
+        assert sv.sv_workspace_bytes(B, g, V) <= limit
+
+
 def test_standardize_validation():
     d = _header_defines()
     lib = sv.load_library()
