@@ -8,15 +8,26 @@ Two input sets generated with different seeds alternate between steps, so
 one step never finds the previous step's rows in the 256 MB last-level cache.
 
 Prints one JSON line: verified sequences/s (value, wall clock over the
-timed steps), the roofline of the call (achieved algorithmic GB/s: bytes per
-call over the mean call time, from two HIP events recorded on the call's
-stream around the timed steps, against 8 TB/s), and the fp64 CPU oracle timed
-on this host's cores on the same inputs.  The timed steps run back to back
-with no event between them; the split of a call between its two launches
-("stages_ms") comes from a separate pass with events around every launch.  The call is one row-stage launch that also
-streams most of the draw (k_main_sample) and a short launch that finishes
-the draw (k_rest_sample); the row and draw work share the first launch, so
-the roofline covers the whole call.
+timed steps, which run back to back with one HIP event pair around all of
+them); the roofline of the dominant kernel, k_main_sample (achieved
+algorithmic GB/s: the call's algorithmic bytes over that launch's mean
+duration, against 8 TB/s), with the same figure for the whole call beside
+it; per-step percentiles; and the fp64 CPU oracle timed on this host's cores
+on the same inputs (all cores, and one thread).  The launch durations and
+the percentiles come from a second pass of the same steps with timing-only
+events recorded on the call's stream before, between and after the two
+launches of every step (in the timed steps those events would cost ~6 us a
+step).  Before the warmup steps, steps run for at least --settle-ms of GPU
+time, so that the clocks have left their idle state whatever --warmup is.
+
+Algorithmic bytes of a call: for every sequence, target rows 0..n_b (the
+rows a left-to-right walk must normalise: "Fast Inference from Transformers
+via Speculative Decoding", Algorithm 1, Phase 3), draft
+row n_b when n_b < gamma (the residual), and the gathers of p and q at the
+gamma drafts.  Target row n_b is counted once; the draw's second read of it
+is this design's extra traffic and shows in the measured traffic, not here.
+All of it is attributed to k_main_sample, the launch that streams the rows
+and most of the draw (k_rest_sample finishes the rest of the draw).
 
 A second, shorter leg times the same call with the acceptance-rate telemetry
 on (beta for every position, alpha): the row stage then streams every target
@@ -94,17 +105,25 @@ class HipEvents:
 
 def cpu_baseline(d: dict, min_wall_s: float) -> dict:
     """The fp64 oracle, untuned, on this host's cores: repeat the whole c4
-    batch until at least ``min_wall_s`` of wall time has passed."""
+    batch until at least ``min_wall_s`` of wall time has passed; then the
+    same on one thread over the batch's first 32 sequences."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.spec_verify_ref(d["target_logits"], d["draft_probs"], d["draft_tokens"],
-                               d["uniforms"], d["temperature"], n_threads=cores, aux=False)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_wall_s and reps >= 2:
-            break
+
+    def timed(nseq, threads):
+        args = (d["target_logits"][:nseq], d["draft_probs"][:nseq], d["draft_tokens"][:nseq],
+                d["uniforms"][:nseq], d["temperature"])
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.spec_verify_ref(*args, n_threads=threads, aux=False)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_wall_s and reps >= 2:
+                return reps, el
+
+    n1 = min(32, d["B"])
+    reps1, el1 = timed(n1, 1)
+    reps, el = timed(d["B"], cores)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -116,7 +135,9 @@ def cpu_baseline(d: dict, min_wall_s: float) -> dict:
         pass
     return {"value": reps * d["B"] / el, "unit": "seqs/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} x the full c4 batch ({d['B']} sequences) in {el:.2f} s wall, "
-                      f"OpenMP over sequences on {cores} threads ({model})"}
+                      f"OpenMP over sequences on {cores} threads ({model})",
+            "value_1thread": reps1 * n1 / el1,
+            "sample_1thread": f"{reps1} x the batch's first {n1} sequences in {el1:.2f} s wall on one thread"}
 
 
 def main():
@@ -127,7 +148,11 @@ def main():
                     help="untimed steps before the timed ones (200 x ~0.11 ms lets the GPU clocks settle)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=2.0,
-                    help="minimum wall time of the CPU-oracle baseline (0 = skip)")
+                    help="minimum wall time of each CPU-oracle baseline figure (0 = skip)")
+    ap.add_argument("--split-steps", type=int, default=100,
+                    help="steps of the pass with per-launch events (split, percentiles; 0 = skip)")
+    ap.add_argument("--settle-ms", type=float, default=40.0,
+                    help="GPU time spent in untimed steps before the warmup steps (clock settling)")
     ap.add_argument("--tele-steps", type=int, default=40,
                     help="timed calls with the acceptance-rate telemetry on (0 = skip)")
     ap.add_argument("--len-steps", type=int, default=40,
@@ -179,15 +204,23 @@ def main():
         torch.cuda.synchronize()
         n_sets.append(n_acc.cpu().numpy().copy())
 
+    # clock settling: untimed steps until --settle-ms of GPU time have run
+    settle_steps = 0
+    if args.settle_ms > 0:
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < args.settle_ms:
+            for i in range(20):
+                step(i)
+            torch.cuda.synchronize()
+            settle_steps += 20
     print("[bench] warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     hev = HipEvents()
-    # the timed region: the steps back to back, one event pair around all of
-    # them on the call's stream (events between the calls would add their
-    # own cost to every call)
+    # the timed region: the steps back to back on the call's stream, one
+    # event pair around all of them
     eb, ee = hev.create(), hev.create()
     print("[bench] timed steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -201,15 +234,15 @@ def main():
     call_ms = hev.elapsed_ms(eb, ee) / args.steps
     hev.destroy(eb)
     hev.destroy(ee)
-    # the split between the two launches, from a separate untimed pass with
-    # events before, between and after the launches of every call
-    nsplit = min(args.steps, 50)
-    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(nsplit)]
-    for i in range(nsplit):
+    # the second pass: timing-only events before, between and after the two
+    # launches of every step (per-launch durations, per-step percentiles)
+    evs = [(hev.create(), hev.create(), hev.create()) for _ in range(args.split_steps)]
+    for i in range(args.split_steps):
         step(i, events=evs[i])
     torch.cuda.synchronize()
     rows_ms = [hev.elapsed_ms(e[0], e[1]) for e in evs]
     draw_ms = [hev.elapsed_ms(e[1], e[2]) for e in evs]
+    step_ms = [hev.elapsed_ms(e[0], e[2]) for e in evs]
     for e in evs:
         for h in e:
             hev.destroy(h)
@@ -219,22 +252,23 @@ def main():
     n_per_step = [n_sets[i % 2] for i in range(args.steps)]
     tokens_per_s = float(sum((n + 1).sum() for n in n_per_step)) / elapsed
 
-    # algorithmic bytes (see the design notes): the row stage must read the
-    # target rows 0..n_b of every sequence; the draw stage reads row n_b of
-    # the target and, when n_b < gamma, row n_b of the draft.
+    # algorithmic bytes (module docstring): target rows 0..n_b once, draft
+    # row n_b when n_b < gamma, the gathers of p and q at the drafts
     s_p = 2
     s_q = 2
-    rows_bytes = [float(((n + 1) * V * s_p).sum() + B * gamma * (s_p + s_q)) for n in n_sets]
-    draw_bytes = [float((V * s_p + (n < gamma) * V * s_q).sum()) for n in n_sets]
-    mean_rows_ms = float(np.mean(rows_ms))
-    mean_draw_ms = float(np.mean(draw_ms))
-    rows_alg_bytes = float(np.mean([rows_bytes[i % 2] for i in range(args.steps)]))
-    draw_alg_bytes = float(np.mean([draw_bytes[i % 2] for i in range(args.steps)]))
-    call_alg_bytes = rows_alg_bytes + draw_alg_bytes
-    achieved = call_alg_bytes / (call_ms * 1e-3) / 1e9
+    alg_sets = [float(((n + 1) * V * s_p).sum() + ((n < gamma) * V * s_q).sum() + B * gamma * (s_p + s_q))
+                for n in n_sets]
+    call_alg_bytes = float(np.mean([alg_sets[i % 2] for i in range(args.steps)]))
+    mean_rows_ms = float(np.mean(rows_ms)) if rows_ms else None
+    mean_draw_ms = float(np.mean(draw_ms)) if draw_ms else None
+    call_achieved = call_alg_bytes / (call_ms * 1e-3) / 1e9
+    # the dominant kernel: k_main_sample's mean duration from the step events
+    main_achieved = call_alg_bytes / (mean_rows_ms * 1e-3) / 1e9 if mean_rows_ms else None
     nominal_bytes = B * G1 * V * s_p + B * gamma * V * s_q
 
-    traffic = None
+    # measured HBM bytes (calibrated FETCH_SIZE + WRITE_SIZE per dispatch,
+    # from the committed rocprofv3 counter runs of this kernel source)
+    traffic = traffic_main = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
@@ -242,6 +276,7 @@ def main():
             sha = hashlib.sha256(f.read()).hexdigest()
         if tr.get("kernel_source_sha256") == sha:
             traffic = tr.get("hbm_bytes_per_call")
+            traffic_main = tr.get("per_kernel_hbm_bytes", {}).get("k_main_sample")
 
     tele = None
     if args.tele_steps > 0:
@@ -278,7 +313,7 @@ def main():
         # 0..gamma-1 and every draft row in the sweep, then the draw rows
         main_b = float(B * G1 * V * s_p + B * gamma * (s_p + s_q))
         sweep_b = float(B * gamma * V * (s_p + s_q))
-        tcall_b = main_b + sweep_b + draw_alg_bytes
+        tcall_b = main_b + sweep_b + float(np.mean([((n < gamma) * V * s_q).sum() for n in n_sets]))
         tcall_ms = 1e3 * tel / args.tele_steps
         sweep_gbps = sweep_b / (t_sweep * 1e-3) / 1e9
         tele = {
@@ -322,7 +357,7 @@ def main():
         hev.destroy(lb)
         hev.destroy(le)
         l_bytes = float(np.mean([((n + 1) * V * s_p).sum() + B * gamma * (s_p + s_q)
-                                 + (V * s_p + (n < gamma) * V * s_q).sum() for n in ln_sets]))
+                                 + ((n < gamma) * V * s_q).sum() for n in ln_sets]))
         lenl = {"lenience": args.lenience, "steps": args.len_steps, "ms_per_step": 1e3 * lel / args.len_steps,
                 "seqs_per_s": B * args.len_steps / lel,
                 "tokens_per_s": float(sum((ln_sets[i % 2] + 1).sum() for i in range(args.len_steps))) / lel,
@@ -444,6 +479,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -453,14 +489,20 @@ def main():
         "config": {"workload": "c4: B=256 gamma=8 V=152064, bf16 target logits + bf16 draft probs, "
                                "T=1.0, z_q~N(0,3^2), z_p=z_q+eps*N(0,1), eps~U(0.2,2.0) per sequence",
                    "batch": int(B), "gamma": int(gamma), "vocab": int(V), "input_dtype": "bf16"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     # the measured bytes (calibrated FETCH_SIZE + WRITE_SIZE of this source) over the same time
-                     "traffic_GBps": None if traffic is None else traffic / (call_ms * 1e-3) / 1e9,
-                     "kernel": "spec_verify call: k_main_sample + k_rest_sample",
-                     "alg_bytes_per_launch": call_alg_bytes, "avg_launch_ms": call_ms},
+        "roofline": None if main_achieved is None else {
+            "bound": "hbm", "achieved": main_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": main_achieved / HBM_PEAK_GBPS, "traffic": traffic_main,
+            "kernel": "k_main_sample", "alg_bytes_per_launch": call_alg_bytes, "avg_launch_ms": mean_rows_ms,
+            "traffic_over_alg": None if traffic_main is None else traffic_main / call_alg_bytes},
+        "call_roofline": {"achieved": call_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": call_achieved / HBM_PEAK_GBPS, "alg_bytes": call_alg_bytes, "avg_call_ms": call_ms,
+                          "traffic": traffic,
+                          "traffic_over_alg": None if traffic is None else traffic / call_alg_bytes},
         "cpu_baseline": cpu,
         "tokens_per_s": tokens_per_s,
+        "step_ms_percentiles": None if not step_ms else {
+            "p10": float(np.percentile(step_ms, 10)), "p50": float(np.percentile(step_ms, 50)),
+            "p90": float(np.percentile(step_ms, 90))},
         "stages_ms": {"main": mean_rows_ms, "rest": mean_draw_ms},
         "hbm_nominal": {"bytes_per_step": nominal_bytes,
                         "GBps": nominal_bytes / (ms_per_step * 1e-3) / 1e9,

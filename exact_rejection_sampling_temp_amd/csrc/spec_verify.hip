@@ -79,16 +79,19 @@ constexpr int kEptFp32 = 32;
 constexpr int kChunkBf16 = kEptBf16 * kThreads;  // 16384 elements
 constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
 
-// Draw geometry.  A sub-chunk is 512 consecutive elements of row n, 8 per
-// lane of one wave; a wave takes 4 consecutive sub-chunks (in passes of 2,
-// which keeps the fused row kernel at 8 waves per SIMD) and a draw chunk
-// (one claim) is the 4 waves of a workgroup: 8192 elements.
-constexpr int kSub = 512;
-constexpr int kSubPerWave = 4;
+// Draw geometry.  A group is 512 consecutive elements of row n, 8 per lane
+// of one wave; a wave task is 4 consecutive groups, a sub-chunk of 2048
+// elements whose sums the wave publishes (loaded in passes of 2 groups in
+// the first launch, which keeps the fused row kernel at 8 waves per SIMD),
+// and a draw chunk (one claim) is the 4 waves of a workgroup: 8192 elements.
+constexpr int kSub = 512;                           // elements of a group
+constexpr int kSubPerWave = 4;                      // groups of a wave task (one sub-chunk)
 constexpr int kSubPerPass = 2;  // first launch (the helpers share SIMDs with the row stage)
-constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16
+constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16 groups in a draw chunk
 constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
-constexpr int kRound = 64 * 8;                      // sub-sums per finish round
+constexpr int kSubW = kSub * kSubPerWave;           // 2048 elements of a sub-chunk
+constexpr int kRPL = 2;                             // sub-chunk sums per lane per finish round
+constexpr int kRound = 64 * kRPL;                   // sub-chunk sums per finish round
 constexpr int kChunkB = 8192;                       // telemetry sweep: row elements per workgroup
 constexpr int kGroupsB = kChunkB / (8 * kThreads);  // groups of 8 per thread
 static_assert(kChunkB == kChunk2, "a telemetry workgroup covers exactly one draw chunk");
@@ -125,16 +128,14 @@ struct SeqCtl {
     uint64_t mask;    // bit k: position k rejected; kInvalidBit: a bad draft token
     uint64_t dec;     // bit k: position k decided (a rejection also sets every
                       // later bit); bit gamma: row gamma's statistics out
-    uint64_t claim;   // low word: draw chunks claimed; high word: claims made
-                      // in the second launch
-    uint64_t cnt2;    // draw wave tasks finished in the second launch, offset
-                      // so that the count reaches kDrawTarget with the last one
+    uint64_t claim;   // draw chunks claimed in the first launch, in order: chunks
+                      // 0 .. claim-1 (claims past nch2 take nothing)
+    uint64_t cnt2;    // draw wave tasks finished in the second launch
     uint64_t retire;  // low word: users done in the second launch; high word:
                       // the sequence's rank in the ready list
     uint64_t pad[3];
 };
 static_assert(sizeof(SeqCtl) == 64, "SeqCtl layout");
-constexpr uint64_t kDrawTarget = 1ull << 40;
 
 struct Layout {
     size_t ctl_off, cnt1_off, ready_off, rcnt_off, control_bytes;
@@ -150,7 +151,7 @@ Layout make_layout(int B, int gamma, int V)
     const size_t rows = (size_t)B * (size_t)(gamma + 1);
     L.nch1_max = (V + kChunkFp32 - 1) / kChunkFp32;
     L.nch2 = (V + kChunk2 - 1) / kChunk2;
-    L.nsub = L.nch2 * kSubPerChunk;
+    L.nsub = L.nch2 * kWaves;  // sub-chunks of kSubW elements
     L.nchb = (V + kChunkB - 1) / kChunkB;
     size_t off = 0;
     L.ctl_off = off;   off = align256(off + sizeof(SeqCtl) * (size_t)B);
@@ -179,6 +180,10 @@ __device__ __forceinline__ double ld_agent_d(const double* p)
 __device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent32(const uint32_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t xchg_agent(uint64_t* p, uint64_t v)
 {
@@ -627,7 +632,7 @@ struct Params {
     uint64_t* cnt1;   // per row: arrivals (low 16 bits), rejection evidence (high 48)
     uint64_t* part1;  // [rows][nch1][2]
     RowStat* stats;   // [rows]
-    SubSum* sub;      // [B][nsub]
+    SubSum* sub;      // [B][nsub] sums of the sub-chunks (kSubW elements) of row n
     uint32_t* ready;  // [B] 1 + the sequences, in the order their n became known
     uint32_t* ready_cnt;
     int32_t* n_out;
@@ -718,17 +723,16 @@ __device__ __forceinline__ bool row_arrive(const Params& p, int64_t row, int b, 
 
 // ------------------------------------------------------------------ draw
 
-// Sums of one wave's 4 sub-chunks s0 .. s0+3 of row n of sequence b, in
-// fp64: E = sum e_v with e_v = 2^((z_v - m) log2(e)/T) (m the row max; the
-// shift -m log2(e)/T is rounded once for the row, a common factor that
-// cancels in every ratio used), and for a residual draw EA, QA over
-// A = {v : e_v > q_v S_row}.  S_row, the row stage's normaliser, only
-// decides membership of A; the exact normaliser is the sum of E.  The sums
-// are published to the sub-chunk slots and the wave counts itself in;
-// returns true (wave-uniform) for the last wave task of the sequence.
+// This lane's share of the sums over groups s0 .. s0+NP-1 of row n of
+// sequence b, in fp64, added to E, EA, QA: E = sum e_v with
+// e_v = 2^((z_v - m) log2(e)/T) (m the row max; the shift -m log2(e)/T is
+// rounded once for the row, a common factor that cancels in every ratio
+// used), and for a residual draw EA, QA over A = {v : e_v > q_v S_row}.
+// S_row, the row stage's normaliser, only decides membership of A; the exact
+// normaliser is the sum of E.
 template <int DT, int PT, bool VEC2, bool RESID, bool FULL, int NP>
 __device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow, const void* qrow, int s0,
-                                               double nMcd, double S_row, double& mE, double& mEA, double& mQA)
+                                               double nMcd, double S_row, double& E, double& EA, double& QA)
 {
     const int lane = threadIdx.x & 63;
     Raw8 zr[NP], qr[NP];
@@ -741,7 +745,6 @@ __device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow
 #pragma unroll
     for (int g = 0; g < NP; ++g) {
         const int idx = (s0 + g) * kSub + lane * 8;
-        double E = 0.0, EA = 0.0, QA = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const bool ok = FULL || idx + e < p.V;
@@ -756,21 +759,16 @@ __device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow
                 QA = fma(qd, in, QA);
             }
         }
-        E = wave_sum(E);
-        if constexpr (RESID) {
-            EA = wave_sum(EA);
-            QA = wave_sum(QA);
-        }
-        if (lane == g) { mE = E; mEA = EA; mQA = QA; }
     }
 }
 
 // COUNTED (second launch): the sums go out with device-scope exchanges and
-// the wave counts itself in; returns true in the wave that completes the
+// the wave counts itself in; returns true in the wave whose count reaches
+// `target` (the sequence's wave tasks in that launch), which completes the
 // sequence's draw sums.  Otherwise (first launch) plain stores, which the
 // second launch reads after the kernel boundary.
 template <int DT, int PT, bool VEC2, bool COUNTED>
-__device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask)
+__device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_t target)
 {
     const int lane = threadIdx.x & 63;
     const int n = first_reject(mask, p.gamma);
@@ -788,35 +786,39 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask)
     const void* qrow = static_cast<const char*>(p.probs) +
                        (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
     // the second launch sits on the critical path with SIMDs to spare: all of
-    // a wave's sub-chunks in one load pass there
+    // a wave's groups in one load pass there
     constexpr int NP = COUNTED ? kSubPerWave : kSubPerPass;
+    double E = 0.0, EA = 0.0, QA = 0.0;  // this lane's share of the sub-chunk's sums
+    if (!(mask & kInvalidBit)) {
 #pragma unroll
-    for (int s = s0; s < s0 + kSubPerWave; s += NP) {
-        double mE = 0.0, mEA = 0.0, mQA = 0.0;  // lane g < NP keeps sub-chunk s + g
-        if (!(mask & kInvalidBit)) {
+        for (int s = s0; s < s0 + kSubPerWave; s += NP) {
             const bool full = (s + NP) * kSub <= p.V;
             if (resid) {
-                if (full) draw_wave_sums<DT, PT, VEC2, true, true, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
-                else draw_wave_sums<DT, PT, VEC2, true, false, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                if (full) draw_wave_sums<DT, PT, VEC2, true, true, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
+                else draw_wave_sums<DT, PT, VEC2, true, false, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
             } else {
-                if (full) draw_wave_sums<DT, PT, VEC2, false, true, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
-                else draw_wave_sums<DT, PT, VEC2, false, false, NP>(p, zrow, qrow, s, nMcd, S_row, mE, mEA, mQA);
+                if (full) draw_wave_sums<DT, PT, VEC2, false, true, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
+                else draw_wave_sums<DT, PT, VEC2, false, false, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
             }
         }
-        if (lane < NP) {
-            if constexpr (COUNTED) {
-                uint64_t* slot = reinterpret_cast<uint64_t*>(p.sub + (size_t)b * p.nsub + s + lane);
-                dep ^= xchg_agent(slot, dbits(mE)) ^ xchg_agent(slot + 1, dbits(mEA)) ^ xchg_agent(slot + 2, dbits(mQA));
-            } else {
-                p.sub[(size_t)b * p.nsub + s + lane] = SubSum{mE, mEA, mQA, 0.0};
-            }
+    }
+    E = wave_sum(E);
+    EA = wave_sum(EA);
+    QA = wave_sum(QA);
+    const int sidx = s0 / kSubPerWave;  // this wave task's sub-chunk
+    if (lane == 0) {
+        if constexpr (COUNTED) {
+            uint64_t* slot = reinterpret_cast<uint64_t*>(p.sub + (size_t)b * p.nsub + sidx);
+            dep ^= xchg_agent(slot, dbits(E)) ^ xchg_agent(slot + 1, dbits(EA)) ^ xchg_agent(slot + 2, dbits(QA));
+        } else {
+            p.sub[(size_t)b * p.nsub + sidx] = SubSum{E, EA, QA, 0.0};
         }
     }
     if constexpr (COUNTED) {
         const uint32_t d = wave_xor(fold64(dep)) & p.zero;
         uint32_t last = 0;
         if (lane == 0) last = __hip_atomic_fetch_add(&p.ctl[b].cnt2, 1ull + d, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT) + 1ull == kDrawTarget ? 1u : 0u;
+                                                     __HIP_MEMORY_SCOPE_AGENT) + 1ull == target ? 1u : 0u;
         return __builtin_amdgcn_readfirstlane(last) != 0u;
     }
     return false;
@@ -834,36 +836,45 @@ __device__ __forceinline__ double draw_weight(const Params& p, bool use_resid, f
 
 // Clears everything the call left in the workspace for sequence b.  Run by
 // one wave, by the sequence's last user.
-__device__ void cleanup_wave(const Params& p, int b, uint32_t rank)
+// Run by one wave, by the sequence's last user.  `listed`: the sequence is
+// in the ready list (sample mode), at `rank`.  It leaves the list first: a
+// second-launch workgroup that reads the control words and then still finds
+// the sequence listed has read them before they were cleared, since every
+// clearing store is issued only once the exchange has returned (its value
+// feeds their addresses).
+__device__ void cleanup_wave(const Params& p, int b, uint32_t rank, bool listed)
 {
     const int lane = threadIdx.x & 63;
     const int G1 = p.gamma + 1;
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < 4) reinterpret_cast<uint4*>(p.ctl + b)[lane] = z4;
-    for (int i = lane; i < G1; i += 64) p.cnt1[(int64_t)b * G1 + i] = 0ull;
-    uint4* part = reinterpret_cast<uint4*>(p.part1 + 2 * (size_t)b * G1 * p.nch1);
-    for (int j = lane; j < G1 * p.nch1; j += 64) part[j] = z4;
-    uint4* st = reinterpret_cast<uint4*>(p.stats + (size_t)b * G1);
-    for (int j = lane; j < 2 * G1; j += 64) st[j] = z4;
-    uint4* ss = reinterpret_cast<uint4*>(p.sub + (size_t)b * p.nsub);
-    for (int j = lane; j < 2 * p.nsub; j += 64) ss[j] = z4;
-    if (lane == 0) {
-        p.ready[rank] = 0u;
-        if (rank == 0) *p.ready_cnt = 0u;
+    uint32_t d = 0;
+    if (listed && lane == 0) {
+        d = __hip_atomic_exchange(&p.ready[rank], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (rank == 0) d ^= __hip_atomic_exchange(p.ready_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    const size_t dz = __builtin_amdgcn_readfirstlane(d) & p.zero;
+    if (lane < 4) reinterpret_cast<uint4*>(p.ctl + b + dz)[lane] = z4;
+    for (int i = lane; i < G1; i += 64) p.cnt1[(int64_t)b * G1 + dz + i] = 0ull;
+    uint4* part = reinterpret_cast<uint4*>(p.part1 + 2 * (size_t)b * G1 * p.nch1 + dz);
+    for (int j = lane; j < G1 * p.nch1; j += 64) part[j] = z4;
+    uint4* st = reinterpret_cast<uint4*>(p.stats + (size_t)b * G1 + dz);
+    for (int j = lane; j < 2 * G1; j += 64) st[j] = z4;
+    uint4* ss = reinterpret_cast<uint4*>(p.sub + (size_t)b * p.nsub + dz);
+    for (int j = lane; j < 2 * p.nsub; j += 64) ss[j] = z4;
 }
 
-// Counts one user of sequence b out in the second launch (each of its nch2
-// workgroups, and the draw); the last of the nch2 + 1 clears the sequence.
-// Called by one wave after its reads of the sequence's workspace.
-__device__ __forceinline__ void retire_wave(const Params& p, int b)
+// Counts one user of sequence b out in the second launch (each of its
+// workgroups with work there, and the draw); the last of the `users` clears
+// the sequence.  Called by one wave after its reads of the sequence's
+// workspace.
+__device__ __forceinline__ void retire_wave(const Params& p, int b, uint32_t users)
 {
     uint64_t old = 0;
     if ((threadIdx.x & 63) == 0)
         old = __hip_atomic_fetch_add(&p.ctl[b].retire, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)old);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(old >> 32));
-    if (lo + 1u == (uint32_t)p.nch2 + 1u) cleanup_wave(p, b, hi);
+    if (lo + 1u == users) cleanup_wave(p, b, hi, true);
 }
 
 // The draw of sequence b and its outputs, by one wave, once every
@@ -871,8 +882,8 @@ __device__ __forceinline__ void retire_wave(const Params& p, int b)
 // rejection, with [ST]'s fallback to p_n; the bonus row p_gamma after full
 // acceptance).  The exact normaliser S and residual mass Z come from the
 // sub-chunk sums; a scan over the sub-chunk weights in index order finds the
-// sub-chunk holding u * total, and a scan of its 512 elements, with every
-// weight recomputed exactly, finds the token.
+// sub-chunk holding u * total, and a scan of its elements, a 512-element
+// group at a time with every weight recomputed exactly, finds the token.
 template <int DT, int PT, bool VEC2>
 __device__ void finish_wave(const Params& p, int b)
 {
@@ -890,11 +901,11 @@ __device__ void finish_wave(const Params& p, int b)
     const double ug = (double)p.uniforms[(int64_t)b * G1 + p.gamma];
     const SubSum* ss = p.sub + (size_t)b * p.nsub;
     const int nrounds = (p.nsub + kRound - 1) / kRound;
-    double rE[8], rEA[8], rQA[8];
+    double rE[kRPL], rEA[kRPL], rQA[kRPL];
     auto load_round = [&](int r) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int j = r * kRound + lane * 8 + i;
+        for (int i = 0; i < kRPL; ++i) {
+            const int j = r * kRound + lane * kRPL + i;
             if (j < p.nsub) {
                 rE[i] = ld_agent_d(&ss[j].E);
                 rEA[i] = ld_agent_d(&ss[j].EA);
@@ -921,7 +932,7 @@ __device__ void finish_wave(const Params& p, int b)
         for (int r = 0; r < nrounds; ++r) {
             if (r > 0) load_round(r);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a += rE[i];
+            for (int i = 0; i < kRPL; ++i) a += rE[i];
         }
         const double S = wave_sum_dpp(a);
         const double invS = 1.0 / S;  // p_v = e_v * invS (within an ulp of e_v / S)
@@ -930,7 +941,7 @@ __device__ void finish_wave(const Params& p, int b)
             for (int r = 0; r < nrounds; ++r) {
                 if (nrounds > 1) load_round(r);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) zl += fmax(0.0, rEA[i] * invS - p.len * rQA[i]);
+                for (int i = 0; i < kRPL; ++i) zl += fmax(0.0, rEA[i] * invS - p.len * rQA[i]);
             }
         }
         Z = wave_sum_dpp(zl);
@@ -949,7 +960,7 @@ __device__ void finish_wave(const Params& p, int b)
             if (nrounds > 1) load_round(r);
             double lt = 0.0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lt += sub_weight(i);
+            for (int i = 0; i < kRPL; ++i) lt += sub_weight(i);
             const double incl = wave_incl_scan_dpp(lt);
             double excl = __shfl_up(incl, 1, 64);
             if (lane == 0) excl = 0.0;
@@ -958,7 +969,7 @@ __device__ void finish_wave(const Params& p, int b)
                 int found = -1, ipos = -1;
                 double c = carry + excl, cpos = c;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < kRPL; ++i) {
                     const double w = sub_weight(i);
                     if (found < 0 && w > 0.0) {
                         if (c + w > target) found = i;
@@ -968,21 +979,22 @@ __device__ void finish_wave(const Params& p, int b)
                 if (found < 0) { found = ipos; c = cpos; }  // rounding: the lane's last positive entry
                 const int f = __shfl(found, L, 64);
                 pre = __shfl(c, L, 64);
-                js = r * kRound + L * 8 + f;
+                js = r * kRound + L * kRPL + f;
             } else {
                 carry += __shfl(incl, 63, 64);
             }
         }
 
-        // scan sub-chunk js (and, only if rounding pushed the crossing out of
-        // it, the sub-chunks after it) in index order, every weight exact
+        // scan sub-chunk js a group (512 elements) at a time (and, only if
+        // rounding pushed the crossing out of it, the groups after it) in
+        // index order, every weight exact
         const int64_t row = (int64_t)b * G1 + n;
         const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
         const void* qrow = static_cast<const char*>(p.probs) +
                            (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
         const double nMcd = -(double)__shfl(st.m, n, 64) * p.cd;  // lane n holds row n's statistics
         double rem = target - pre;
-        for (int s = js; js >= 0 && s < p.nsub && t < 0; ++s) {
+        for (int s = js * kSubPerWave; js >= 0 && s < p.nsub * kSubPerWave && t < 0; ++s) {
             const int idx = s * kSub + lane * 8;
             if (s * kSub >= p.V) break;
             const Raw8 zr = load_group<DT, VEC2>(zrow, idx, p.V);
@@ -1024,8 +1036,8 @@ __device__ void finish_wave(const Params& p, int b)
             for (int r = 0; r < nrounds; ++r) {
                 if (nrounds > 1) load_round(r);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (sub_weight(i) > 0.0) jl = r * kRound + lane * 8 + i;
+                for (int i = 0; i < kRPL; ++i)
+                    if (sub_weight(i) > 0.0) jl = r * kRound + lane * kRPL + i;
             }
             jl = wave_max_i(jl);
             auto scan_back = [&](int from, bool wres) {
@@ -1046,11 +1058,11 @@ __device__ void finish_wave(const Params& p, int b)
                 }
                 return -1;
             };
-            t = scan_back(jl, use_resid);
+            t = scan_back(jl * kSubPerWave + kSubPerWave - 1, use_resid);
             // (the residual support is chosen with the row stage's
             // normaliser; should no element of it survive the exact one, the
             // row n itself, which always has an element with e_v = 1)
-            if (t < 0) t = scan_back(p.nsub - 1, false);
+            if (t < 0) t = scan_back(p.nsub * kSubPerWave - 1, false);
         }
     }
 
@@ -1081,10 +1093,10 @@ __device__ void finish_wave(const Params& p, int b)
 // sub-chunks c2 * 16 + 4w .. +3.  No workgroup barrier inside.  COUNTED:
 // see draw_wave; returns true in the wave that completes the sequence.
 template <int DT, int PT, bool VEC2, bool COUNTED>
-__device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint64_t mask)
+__device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint64_t mask, uint64_t target = 0)
 {
     const int w = threadIdx.x >> 6;
-    return draw_wave<DT, PT, VEC2, COUNTED>(p, b, c2 * kSubPerChunk + w * kSubPerWave, mask);
+    return draw_wave<DT, PT, VEC2, COUNTED>(p, b, c2 * kSubPerChunk + w * kSubPerWave, mask, target);
 }
 
 // ------------------------------------------------------------ sample, launch 1
@@ -1449,50 +1461,47 @@ __global__ __launch_bounds__(kThreads) void k_beta_merge(const Params p)
 
 // ------------------------------------------------------------ sample, launch 2
 
-// nch2 workgroups per sequence: they take the draw chunks the first launch
-// left, and the wave that completes a sequence's draw sums runs its draw.
-// Workgroup i < B serves the sequence whose n became known (B-1-i)-th, the
-// rest (nch2 - 1 per sequence) follow in the same order: the first claim of
-// every sequence comes early, and the sequences resolved last, which have
-// the most unclaimed chunks, are served first.  A sequence's first claim in
-// this launch learns how many chunks are left (the first launch took the
-// ones before it) and offsets the completion count so that the last of
-// their wave tasks -- or this claim itself, when none is left -- brings it to
-// kDrawTarget.  The last of the sequence's users here clears its workspace.
+// nch2 workgroups per sequence.  The first launch's helpers took draw
+// chunks 0 .. L1-1 of a sequence (its claim count, final now); chunk L1 + j
+// goes to the sequence's workgroup j, and a workgroup with no chunk left
+// returns after reading that count.  Workgroup i < B is workgroup 0 of the
+// sequence whose n became known (B-1-i)-th; the others (nch2 - 1 per
+// sequence) follow in the same order, so the sequences resolved last, which
+// have the most chunks left, are served first.  The wave that completes the
+// sequence's remaining wave tasks (workgroup 0 itself when none is left) runs
+// the draw; the last of the sequence's users here (its workgroups with a
+// chunk, and the draw) clears its workspace.
 template <int DT, int PT, bool VEC2>
 __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
 {
     const int i = (int)blockIdx.x;
-    const int r = p.B - 1 - (i < p.B ? i : (i - p.B) / max(p.nch2 - 1, 1));
-    const int b = (int)p.ready[r] - 1;
-    if (b < 0 || b >= p.B) return;  // (every sequence is in the list once launch 1 is done)
-    __shared__ int sm_cmd;
-    __shared__ int sm_fin;
-    __shared__ uint64_t sm_mask;
-    if (threadIdx.x == 0) {
-        const uint64_t old = add_agent64(&p.ctl[b].claim, 1ull + (1ull << 32));
-        const uint32_t cl = (uint32_t)old;
-        int fin = 0;
-        if ((old >> 32) == 0) {
-            const uint64_t left = cl < (uint32_t)p.nch2 ? (uint64_t)(p.nch2 - (int)cl) : 0ull;
-            const uint64_t add = kDrawTarget - (uint64_t)kWaves * left;
-            const uint64_t o2 = __hip_atomic_fetch_add(&p.ctl[b].cnt2, add, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-            fin = o2 + add == kDrawTarget ? 1 : 0;
-        }
-        sm_cmd = cl < (uint32_t)p.nch2 ? (int)cl : -1;
-        sm_fin = fin;
-        sm_mask = p.ctl[b].mask;  // final: the row stage has finished
-    }
-    __syncthreads();
-    bool fin_wave = sm_fin && threadIdx.x < 64;
-    if (sm_cmd >= 0 && draw_chunk<DT, PT, VEC2, true>(p, b, sm_cmd, sm_mask)) fin_wave = true;
+    const int per = max(p.nch2 - 1, 1);
+    const int r = p.B - 1 - (i < p.B ? i : (i - p.B) / per);
+    const int j = i < p.B ? 0 : 1 + (i - p.B) % per;
+    // (every sequence is in the list once launch 1 is done, and leaves it when
+    // the last of its users here clears its workspace)
+    const uint32_t listed = ld_agent32(&p.ready[r]);
+    const int b = (int)listed - 1;
+    if (b < 0 || b >= p.B) return;
+    // the first launch's claim count, final during this launch -- unless the
+    // sequence has been cleared meanwhile, in which case it is no longer
+    // listed and this workgroup had nothing to do
+    const uint64_t claim = ld_agent(&p.ctl[b].claim);
+    if (ld_agent32(&p.ready[r] + (fold64(claim) & p.zero)) != listed) return;
+    const int l1 = (int)min((uint32_t)claim, (uint32_t)p.nch2);
+    const int left = p.nch2 - l1;
+    const int users = max(left, 1);  // workgroups of the sequence with work here
+    if (j >= users) return;
+    const uint64_t mask = ld_agent(&p.ctl[b].mask);  // final: the row stage has finished
+    bool fin_wave = false;
+    if (left == 0) fin_wave = threadIdx.x < 64;  // nothing left: workgroup 0 draws
+    else if (draw_chunk<DT, PT, VEC2, true>(p, b, l1 + j, mask, (uint64_t)kWaves * left)) fin_wave = true;
     if (fin_wave) {
         finish_wave<DT, PT, VEC2>(p, b);
-        retire_wave(p, b);
+        retire_wave(p, b, (uint32_t)users + 1u);
     }
     __syncthreads();  // this workgroup's work is done
-    if (threadIdx.x < 64) retire_wave(p, b);
+    if (threadIdx.x < 64) retire_wave(p, b, (uint32_t)users + 1u);
 }
 
 // ----------------------------------------------------------------- greedy mode
@@ -1626,7 +1635,7 @@ __global__ __launch_bounds__(kThreads) void k_draw_greedy(const Params p)
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = NAN;
     }
-    cleanup_wave(p, b, 0u);  // (no ready list in greedy mode)
+    cleanup_wave(p, b, 0u, false);  // (no ready list in greedy mode)
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t ntail)

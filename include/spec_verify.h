@@ -225,7 +225,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
  * and after SV_ERR_LAUNCH the array must be considered dirty (later calls
  * may give wrong results).  Returns SV_ERR_SCRATCH, without launching
  * anything, when sv_workspace_bytes(batch, gamma, vocab) exceeds the array
- * (batch up to 594 at gamma 8 and vocab 152 064 fits, and up to 280 at
+ * (batch up to 1231 at gamma 8 and vocab 152 064 fits, and up to 475 at
  * gamma 16 and vocab 256 000).  Every other argument, the results and the status codes as for
  * spec_verify_lenient.
  */

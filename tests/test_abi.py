@@ -152,13 +152,13 @@ def test_noalloc_entry_point_validation():
     assert call(l=1.5) == d["SV_ERR_LENIENCE"]
     assert call(logits=None) == d["SV_ERR_NULL_POINTER"]
     assert call(logits=FAKE + 1) == d["SV_ERR_ALIGNMENT"]
-    # 1024 x 9 rows of 152064 need about 13.8 MiB of workspace: more than the 8 MiB array
+    # 4096 x 9 rows of 152064 need about 27 MiB of workspace: more than the 8 MiB array
     m = re.search(r"#define\s+SV_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", _header_text())
     limit = int(m.group(1)) << int(m.group(2))
     assert limit == 8 << 20
-    assert sv.sv_workspace_bytes(1024, 8, 152_064) > limit
-    assert call(B=1024, gamma=8, V=152_064) == d["SV_ERR_SCRATCH"]
-    assert call(B=1024, gamma=8, V=152_064, mode=sv.SV_GREEDY) == d["SV_ERR_SCRATCH"]
+    assert sv.sv_workspace_bytes(4096, 8, 152_064) > limit
+    assert call(B=4096, gamma=8, V=152_064) == d["SV_ERR_SCRATCH"]
+    assert call(B=4096, gamma=8, V=152_064, mode=sv.SV_GREEDY) == d["SV_ERR_SCRATCH"]
     # every shape the benchmark and the tests use fits
     for B, g, V in ((1, 4, 8), (8, 4, 32_000), (64, 4, 128_256), (256, 8, 152_064), (32, 16, 256_000)):
         assert sv.sv_workspace_bytes(B, g, V) <= limit

@@ -98,9 +98,9 @@ def test_noalloc_allocates_nothing_and_rejects_too_large():
     compare({"n_accepted": n.cpu().numpy(), "out_tokens": out.cpu().numpy()}, r, gamma,
             draft_tokens=d["draft_tokens"], vocab=d["V"])
     # a batch whose workspace exceeds the array is refused before any launch
-    big = torch.empty((1024, 9, 152_064), dtype=torch.bfloat16, device="cuda")
+    big = torch.empty((4096, 9, 152_064), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(sv.SpecVerifyError) as e:
-        sv.spec_verify_noalloc(big, None, torch.zeros((1024, 8), dtype=torch.int32, device="cuda"), None,
+        sv.spec_verify_noalloc(big, None, torch.zeros((4096, 8), dtype=torch.int32, device="cuda"), None,
                                1.0, "greedy")
     assert "scratch" in str(e.value)
     del big
