@@ -730,18 +730,23 @@ __device__ __forceinline__ bool row_arrive(const Params& p, int64_t row, int b, 
 // used), and for a residual draw EA, QA over A = {v : e_v > q_v S_row}.
 // S_row, the row stage's normaliser, only decides membership of A; the exact
 // normaliser is the sum of E.
-template <int DT, int PT, bool VEC2, bool RESID, bool FULL, int NP>
-__device__ __forceinline__ void draw_wave_sums(const Params& p, const void* zrow, const void* qrow, int s0,
-                                               double nMcd, double S_row, double& E, double& EA, double& QA)
+template <int DT, int PT, bool VEC2, int NP>
+__device__ __forceinline__ void draw_wave_load(const Params& p, const void* zrow, const void* qrow, bool resid,
+                                               int s0, Raw8 (&zr)[NP], Raw8 (&qr)[NP])
 {
     const int lane = threadIdx.x & 63;
-    Raw8 zr[NP], qr[NP];
 #pragma unroll
     for (int g = 0; g < NP; ++g) zr[g] = load_group<DT, VEC2>(zrow, (s0 + g) * kSub + lane * 8, p.V);
-    if constexpr (RESID) {
+    if (resid) {
 #pragma unroll
         for (int g = 0; g < NP; ++g) qr[g] = load_group<PT, VEC2>(qrow, (s0 + g) * kSub + lane * 8, p.V);
     }
+}
+template <int DT, int PT, bool VEC2, bool RESID, bool FULL, int NP>
+__device__ __forceinline__ void draw_wave_sums(const Params& p, const Raw8 (&zr)[NP], const Raw8 (&qr)[NP], int s0,
+                                               double nMcd, double S_row, double& E, double& EA, double& QA)
+{
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int g = 0; g < NP; ++g) {
         const int idx = (s0 + g) * kSub + lane * 8;
@@ -775,13 +780,6 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_
     const bool resid = n < p.gamma;
     const int64_t row = (int64_t)b * (p.gamma + 1) + n;
     uint64_t dep = 0;
-    double nMcd = 0.0, S_row = 0.0;
-    if (!(mask & kInvalidBit)) {
-        const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
-        nMcd = -(double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
-        // (only decides membership of A = {v : e_v > l q_v S}: scaled by the lenience)
-        S_row = p.len * __longlong_as_double((long long)ld_agent(sw + 1));
-    }
     const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
     const void* qrow = static_cast<const char*>(p.probs) +
                        (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
@@ -790,15 +788,24 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_
     constexpr int NP = COUNTED ? kSubPerWave : kSubPerPass;
     double E = 0.0, EA = 0.0, QA = 0.0;  // this lane's share of the sub-chunk's sums
     if (!(mask & kInvalidBit)) {
+        // the first pass's elements are on their way before the row's
+        // statistics are asked for
+        Raw8 zr[NP], qr[NP];
+        draw_wave_load<DT, PT, VEC2, NP>(p, zrow, qrow, resid, s0, zr, qr);
+        const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
+        const double nMcd = -(double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
+        // (only decides membership of A = {v : e_v > l q_v S}: scaled by the lenience)
+        const double S_row = p.len * __longlong_as_double((long long)ld_agent(sw + 1));
 #pragma unroll
         for (int s = s0; s < s0 + kSubPerWave; s += NP) {
+            if (s > s0) draw_wave_load<DT, PT, VEC2, NP>(p, zrow, qrow, resid, s, zr, qr);
             const bool full = (s + NP) * kSub <= p.V;
             if (resid) {
-                if (full) draw_wave_sums<DT, PT, VEC2, true, true, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
-                else draw_wave_sums<DT, PT, VEC2, true, false, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
+                if (full) draw_wave_sums<DT, PT, VEC2, true, true, NP>(p, zr, qr, s, nMcd, S_row, E, EA, QA);
+                else draw_wave_sums<DT, PT, VEC2, true, false, NP>(p, zr, qr, s, nMcd, S_row, E, EA, QA);
             } else {
-                if (full) draw_wave_sums<DT, PT, VEC2, false, true, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
-                else draw_wave_sums<DT, PT, VEC2, false, false, NP>(p, zrow, qrow, s, nMcd, S_row, E, EA, QA);
+                if (full) draw_wave_sums<DT, PT, VEC2, false, true, NP>(p, zr, qr, s, nMcd, S_row, E, EA, QA);
+                else draw_wave_sums<DT, PT, VEC2, false, false, NP>(p, zr, qr, s, nMcd, S_row, E, EA, QA);
             }
         }
     }
@@ -994,12 +1001,29 @@ __device__ void finish_wave(const Params& p, int b)
                            (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
         const double nMcd = -(double)__shfl(st.m, n, 64) * p.cd;  // lane n holds row n's statistics
         double rem = target - pre;
+        // the sub-chunk's groups, all loads in flight at once
+        Raw8 zs[kSubPerWave], qs[kSubPerWave];
+        if (js >= 0) {
+#pragma unroll
+            for (int g = 0; g < kSubPerWave; ++g) {
+                zs[g] = load_group<DT, VEC2>(zrow, (js * kSubPerWave + g) * kSub + lane * 8, p.V);
+                if (use_resid) qs[g] = load_group<PT, VEC2>(qrow, (js * kSubPerWave + g) * kSub + lane * 8, p.V);
+            }
+        }
         for (int s = js * kSubPerWave; js >= 0 && s < p.nsub * kSubPerWave && t < 0; ++s) {
             const int idx = s * kSub + lane * 8;
             if (s * kSub >= p.V) break;
-            const Raw8 zr = load_group<DT, VEC2>(zrow, idx, p.V);
-            Raw8 qr{};
-            if (use_resid) qr = load_group<PT, VEC2>(qrow, idx, p.V);
+            const int g = s - js * kSubPerWave;
+            Raw8 zr{}, qr{};
+            if (g < kSubPerWave) {
+                // (a constant index into the prefetched groups)
+#pragma unroll
+                for (int h = 0; h < kSubPerWave; ++h)
+                    if (h == g) { zr = zs[h]; qr = qs[h]; }
+            } else {
+                zr = load_group<DT, VEC2>(zrow, idx, p.V);
+                if (use_resid) qr = load_group<PT, VEC2>(qrow, idx, p.V);
+            }
             double w[8], lt = 0.0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1487,12 +1511,12 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
     // sequence has been cleared meanwhile, in which case it is no longer
     // listed and this workgroup had nothing to do
     const uint64_t claim = ld_agent(&p.ctl[b].claim);
-    if (ld_agent32(&p.ready[r] + (fold64(claim) & p.zero)) != listed) return;
+    const uint64_t mask = ld_agent(&p.ctl[b].mask);  // final too: the row stage has finished
+    if (ld_agent32(&p.ready[r] + (fold64(claim ^ mask) & p.zero)) != listed) return;
     const int l1 = (int)min((uint32_t)claim, (uint32_t)p.nch2);
     const int left = p.nch2 - l1;
     const int users = max(left, 1);  // workgroups of the sequence with work here
     if (j >= users) return;
-    const uint64_t mask = ld_agent(&p.ctl[b].mask);  // final: the row stage has finished
     bool fin_wave = false;
     if (left == 0) fin_wave = threadIdx.x < 64;  // nothing left: workgroup 0 draws
     else if (draw_chunk<DT, PT, VEC2, true>(p, b, l1 + j, mask, (uint64_t)kWaves * left)) fin_wave = true;
