@@ -370,7 +370,7 @@ def main():
         print("[bench] driver leg", file=sys.stderr, flush=True)
         from exact_rejection_sampling_temp_amd import driver
         c_cost = 0.05
-        models, _ = synth.make_position_models(args.driver_len + 64, V, seed=21, dtype=synth.BF16, sigma=3.0,
+        models = synth.make_position_models(args.driver_len + 64, V, seed=21, dtype=synth.BF16, sigma=3.0,
                                                shift=1.0)
         alpha_m = driver.estimate_alpha(models, np.arange(16))
         g_star = driver.optimal_gamma(alpha_m, c_cost)

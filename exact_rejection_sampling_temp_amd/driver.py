@@ -4,9 +4,10 @@ The orchestration loop around the verify step ("Fast Inference from
 Transformers via Speculative Decoding", summary page, the system overview's
 "Orchestration Loop": each iteration drafts gamma tokens, verifies them with
 one parallel target evaluation, and extends the prefix by n + 1 tokens; the
-KV-cache rollback of "The exact decoding shortcut that burns compute when
-guesses miss", "Production Engineering Takeaways": after a rejection at k the
-sequence's length pointer becomes base + k + 1 and nothing else is undone).
+KV-cache rollback of "Speculative Decoding Paper Breakdown: Lossless
+Draft-and-Verify Acceleration for Autoregressive Transformers", section 5,
+"Production Engineering Takeaways": after a rejection at k the sequence's
+length pointer becomes base + k + 1 and nothing else is undone).
 
 The "models" here are position-only: the target's logits and the draft's
 probabilities at absolute position t do not depend on the tokens before t.

@@ -232,7 +232,7 @@ def make_position_models(L: int, V: int, seed: int, dtype: str = FP32, T: float 
     for each absolute position t, z_q[t] ~ N(0, sigma^2), z_p[t] = z_q[t] +
     shift * N(0, 1); q[t] = softmax(z_q[t] / T) in fp64 (the draft's output),
     cast to ``dtype``.  ``iid``: one row pair for every position.  Returns the
-    driver's PositionOnlyModels plus the fp64 target rows for the checks."""
+    driver's PositionOnlyModels."""
     from exact_rejection_sampling_temp_amd.driver import PositionOnlyModels
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0xF4]))
     n = 1 if iid else L
@@ -243,11 +243,8 @@ def make_position_models(L: int, V: int, seed: int, dtype: str = FP32, T: float 
         zp = np.repeat(zp, L, 0)
     q64 = _softmax64(zq, T)
     zp_c = _cast(zp, dtype)
-    zp_used = zp_c.astype(np.float64) if dtype == FP32 else bf16_bits_to_f32(zp_c).astype(np.float64)
-    p64 = _softmax64(zp_used, T)
-    m = PositionOnlyModels(target_logits=np.ascontiguousarray(zp_c), draft_probs=_cast(q64, dtype),
-                           draft_probs64=q64, temperature=T)
-    return m, p64
+    return PositionOnlyModels(target_logits=np.ascontiguousarray(zp_c), draft_probs=_cast(q64, dtype),
+                              draft_probs64=q64, temperature=T)
 
 
 def standardize_draft_topk(d: dict, k: int, seed: int) -> dict:

@@ -17,6 +17,7 @@ import oracle
 from oracle import analysis
 from exact_rejection_sampling_temp_amd import driver
 from tests import synth
+from tests.laws import target_law
 
 
 class OracleVerifier:
@@ -80,7 +81,8 @@ def test_streams_follow_p_at_every_position():
     """20 000 streams of 10 tokens, V = 6, gamma = 3: the token at each
     position is distributed as p_t (chi-square per position, fixed seed)."""
     L, V, gamma = 10, 6, 3
-    m, p64 = synth.make_position_models(L + gamma, V, seed=3)
+    m = synth.make_position_models(L + gamma, V, seed=3)
+    p64 = target_law(m)
     r = driver.speculative_decode(m, 20_000, L, gamma, seed=4, verify=OracleVerifier(m))
     tok = r["tokens"]
     assert np.all(tok >= 0)
@@ -96,7 +98,8 @@ def test_tokens_per_iteration_match_equation_1(gamma):
     """Same rows at every position: mean tokens per iteration within 4 sigma
     of (1 - alpha^(gamma+1)) / (1 - alpha), alpha = sum min(p, q)."""
     L, V = 40, 8
-    m, p64 = synth.make_position_models(L + gamma, V, seed=5, iid=True)
+    m = synth.make_position_models(L + gamma, V, seed=5, iid=True)
+    p64 = target_law(m)
     alpha = analysis.acceptance_rate(p64[0], m.draft_probs.astype(np.float64)[0])
     r = driver.speculative_decode(m, 3000, L, gamma, seed=6, verify=OracleVerifier(m))
     k = np.concatenate(r["accepted"]).astype(float) + 1.0
@@ -110,7 +113,8 @@ def test_lenient_driver_bounds_each_position_by_p_over_l():
     """With lenience l the emitted law at each position stays below p_t / l
     (the page's guarantee) and accepts more per iteration."""
     L, V, gamma, l = 6, 5, 2, 0.5
-    m, p64 = synth.make_position_models(L + gamma, V, seed=7)
+    m = synth.make_position_models(L + gamma, V, seed=7)
+    p64 = target_law(m)
     r = driver.speculative_decode(m, 20_000, L, gamma, seed=8, verify=OracleVerifier(m), lenience=l)
     r1 = driver.speculative_decode(m, 20_000, L, gamma, seed=8, verify=OracleVerifier(m))
     for t in range(L):
