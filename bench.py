@@ -27,7 +27,8 @@ row n_b when n_b < gamma (the residual), and the gathers of p and q at the
 gamma drafts.  Target row n_b is counted once; the draw's second read of it
 is this design's extra traffic and shows in the measured traffic, not here.
 All of it is attributed to k_main_sample, the launch that streams the rows
-and most of the draw (k_rest_sample finishes the rest of the draw).
+and, with its appended draw helpers, most of the draw (k_finish_sample computes
+the chunks no helper took and the draw itself).
 
 A second, shorter leg times the same call with the acceptance-rate telemetry
 on (beta for every position, alpha): the row stage then streams every target

@@ -23,7 +23,7 @@ SV_FP32 = 0
 SV_BF16 = 1
 SV_SAMPLE = 0
 SV_GREEDY = 1
-SV_MAX_GAMMA = 62
+SV_MAX_GAMMA = 63
 SV_OK = 0
 SV_TOPK = 0
 SV_TOPP = 1

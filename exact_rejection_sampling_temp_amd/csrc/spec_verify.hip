@@ -95,13 +95,10 @@ constexpr int kRound = 64 * kRPL;                   // sub-chunk sums per finish
 constexpr int kChunkB = 8192;                       // telemetry sweep: row elements per workgroup
 constexpr int kGroupsB = kChunkB / (8 * kThreads);  // groups of 8 per thread
 static_assert(kChunkB == kChunk2, "a telemetry workgroup covers exactly one draw chunk");
-// Workgroups of the row stage that find their row unneeded take draw chunks
-// from this position on (earlier positions stream while most of the rows
-// are still needed, and HBM is the shared bottleneck then).
-#ifndef SV_HELP_FROM
-#define SV_HELP_FROM 3
-#endif
-constexpr int kHelpFrom = SV_HELP_FROM;
+static_assert(kChunk2 == kSubW * kWaves, "a draw chunk is one sub-chunk per wave");
+// Bound of a draw helper's wait for its sequence to be resolved (polls ~1 us
+// apart under load; the row stage of a call takes ~100 us at most).
+constexpr int kHelpPolls = 1 << 14;
 
 
 // Per-row statistics written by the row stage.
@@ -652,6 +649,8 @@ struct Params {
     double cd;         // log2(e)/T in double
     double len;        // lenience l in [0, 1] (1: the exact method)
     Exp2Coef ex;       // kExp2Coef
+    int rows_grid;     // first launch: row blocks (G1 * B * nch1); the draw helpers follow
+    int help_polls;    // bound of a draw helper's wait for its sequence
     int polls_slot;    // bound of a merge's wait for a partial slot
     int drop_slot;     // test hook: >= 0 makes chunk 0 of that position withhold its
                        // partial, so that the merge's bounded wait runs out
@@ -1125,6 +1124,45 @@ __device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint6
 
 // ------------------------------------------------------------ sample, launch 1
 
+// Draw helpers, appended to the first launch's grid after every row block:
+// helper j serves the sequence whose n became known (j / nch2)-th.  It waits,
+// bounded, until that sequence is in the ready list, then claims one of its
+// draw chunks and computes the chunk's sums.  Being dispatched after every
+// row block, the helpers take no slot from the rows of any position, and they
+// wait only on row blocks, which never wait on them.  A helper whose wait runs
+// out leaves its chunk to the last launch.
+template <int DT, int PT, bool VEC2>
+__device__ void help_draw(const Params& p, int j)
+{
+    __shared__ int sm_hb, sm_hc;
+    __shared__ uint64_t sm_hm;
+    const int r = j / p.nch2;
+    if (threadIdx.x == 0) {
+        int hb = -1, hc = -1;
+        for (int it = 0; it < p.help_polls; ++it) {
+            const uint32_t e = ld_agent32(&p.ready[r]);
+            if (e != 0u) {
+                hb = (int)e - 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (hb >= 0 && hb < p.B) {
+            const uint32_t cl = (uint32_t)add_agent64(&p.ctl[hb].claim, 1ull);
+            if (cl < (uint32_t)p.nch2) {
+                hc = (int)cl;
+                // read once the sequence is listed: every reject bit up to n,
+                // and row n's statistics, were published before it was
+                sm_hm = ld_agent(&p.ctl[hb].mask + (cl & p.zero));
+            }
+        }
+        sm_hb = hb;
+        sm_hc = hc;
+    }
+    __syncthreads();
+    if (sm_hc >= 0) draw_chunk<DT, PT, VEC2, false>(p, sm_hb, sm_hc, sm_hm);
+}
+
 // Decision inputs read through the scalar cache: every lane of the workgroup
 // asks for the same address and the inputs are read-only during the call.
 // The scalar counter is separate from the vector one, so waiting for the
@@ -1181,6 +1219,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
     constexpr bool VEC = VMODE >= 1, VEC2 = VMODE == 2;
     constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
     constexpr int CH = EPT * kThreads;
+    if (blockIdx.x >= (unsigned)p.rows_grid) {
+        help_draw<DT, PT, VEC2>(p, (int)(blockIdx.x - (unsigned)p.rows_grid));
+        return;
+    }
     const int c = (int)(blockIdx.x % (unsigned)p.nch1);
     const int t = (int)(blockIdx.x / (unsigned)p.nch1);
     const int b = t % p.B;
@@ -1192,7 +1234,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
     __shared__ int sm_i[kWaves];
     __shared__ double sm_d[kWaves];
     __shared__ int sm_cmd;
-    __shared__ uint64_t sm_mask;
 
     // The decision inputs (draft token, uniform, then the token's logit and
     // draft probability) are fetched in case this block turns out to be the
@@ -1204,39 +1245,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
     float uk = 0.0f;
     if (k > 0 && k < p.gamma) fetch_token_uniform(p, b, k, xk, uk);
     if (k > 0 && !p.tele) {
-        // Is this row still needed?  If an earlier position was rejected it
-        // is not; then, once every position up to the first rejection is
-        // decided, claim a draw chunk of the sequence instead.
-        if (threadIdx.x == 0) {
-            int cmd = -2;  // -2: stream the row chunk, -1: nothing, >= 0: draw chunk
-            const uint64_t m = ld_agent(&p.ctl[b].mask);
-            const uint64_t d = ld_agent(&p.ctl[b].dec);
-            const uint64_t cl0 = ld_agent(&p.ctl[b].claim);
-            // Only a reject bit below k makes row k unneeded.  A bad draft
-            // token at position j sets kInvalidBit together with reject bit
-            // j, so rows past j skip while every row before j is still
-            // streamed and decided: each position of the sequence then gets
-            // a decision bit, and its last user clears the workspace.
-            if (m & ((1ull << k) - 1ull)) {
-                cmd = -1;
-                const uint64_t all = rows_mask(p.gamma);
-                if (k >= kHelpFrom && (d & all) == all && (uint32_t)cl0 < (uint32_t)p.nch2) {
-                    const uint32_t cl = (uint32_t)add_agent64(&p.ctl[b].claim, 1ull);
-                    // re-read after dec: every reject bit announced by dec is
-                    // in this value
-                    const uint64_t m2 = ld_agent(&p.ctl[b].mask);
-                    if (cl < (uint32_t)p.nch2) { cmd = (int)cl; sm_mask = m2; }
-                }
-            }
-            sm_cmd = cmd;
-        }
+        // Is this row still needed?  Only a reject bit below k makes row k
+        // unneeded.  A bad draft token at position j sets kInvalidBit
+        // together with reject bit j, so rows past j skip while every row
+        // before j is still streamed and decided: each position of the
+        // sequence then gets a decision bit.
+        if (threadIdx.x == 0) sm_cmd = (ld_agent(&p.ctl[b].mask) & ((1ull << k) - 1ull)) ? 1 : 0;
         __syncthreads();
-        const int cmd = sm_cmd;
-        if (cmd != -2) {
-            // (the draw itself waits for the second launch)
-            if (cmd >= 0) draw_chunk<DT, PT, VEC2, false>(p, b, cmd, sm_mask);
-            return;
-        }
+        if (sm_cmd) return;
     }
     uint32_t zw = 0, qw = 0, zsel = 0, qsel = 0;
     uint32_t dep = 0;
@@ -1526,6 +1542,28 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
     }
     __syncthreads();  // this workgroup's work is done
     if (threadIdx.x < 64) retire_wave(p, b, (uint32_t)users + 1u);
+}
+
+// The last launch when the first launch carries draw helpers: one workgroup
+// per sequence, the sequence resolved last first.  It computes the draw
+// chunks no helper took (chunks L1 .. nch2-1, L1 the claim count), runs the
+// draw and clears the sequence.
+template <int DT, int PT, bool VEC2>
+__global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
+{
+    const int r = p.B - 1 - (int)blockIdx.x;
+    const int b = (int)p.ready[r] - 1;
+    if (b < 0 || b >= p.B) return;  // (every sequence is in the list once launch 1 is done)
+    // the first launch is over: its claim count and the reject mask are final
+    const int l1 = (int)min((uint32_t)p.ctl[b].claim, (uint32_t)p.nch2);
+    const int left = p.nch2 - l1;
+    const uint64_t mask = p.ctl[b].mask;
+    bool fin_wave = left == 0 && threadIdx.x < 64;  // nothing left: wave 0 draws
+    for (int c2 = l1; c2 < p.nch2; ++c2)
+        if (draw_chunk<DT, PT, VEC2, true>(p, b, c2, mask, (uint64_t)kWaves * left)) fin_wave = true;
+    if (fin_wave) finish_wave<DT, PT, VEC2>(p, b);
+    __syncthreads();  // the draw's reads are done
+    if (threadIdx.x < 64) cleanup_wave(p, b, (uint32_t)r, true);
 }
 
 // ----------------------------------------------------------------- greedy mode
@@ -2060,8 +2098,13 @@ void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream
         if (hipGetLastError() != hipSuccess) { *ok = false; return; }
         if (ev_tele && hipEventRecord(ev_tele, s) != hipSuccess) { *ok = false; return; }
     }
-    if (vmode == 2) hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
+    if (p.tele) {
+        if (vmode == 2) hipLaunchKernelGGL((k_rest_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_rest_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
+    } else {
+        if (vmode == 2) hipLaunchKernelGGL((k_finish_sample<DT, PT, true>), dim3(grid2), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_finish_sample<DT, PT, false>), dim3(grid2), dim3(kThreads), 0, s, p);
+    }
     if (hipGetLastError() != hipSuccess) *ok = false;
 }
 
@@ -2218,7 +2261,11 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     const long long grid2 = greedy ? (long long)batch : (long long)batch * L.nch2;
     const bool tele = !greedy && extras && (extras->beta || extras->alpha);
     const long long gridb = tele ? (long long)batch * gamma * L.nchb : 0;
-    if (nch1 > 0xffff || grid1 > INT_MAX || grid2 > INT_MAX || gridb > INT_MAX) return SV_ERR_TOO_LARGE;
+    // sample mode without telemetry: draw helpers follow the row blocks of
+    // the first launch, and the last launch is one workgroup per sequence
+    const bool helpers = !greedy && !tele;
+    const long long gridh = helpers ? grid1 + (long long)batch * L.nch2 : grid1;
+    if (nch1 > 0xffff || gridh > INT_MAX || grid2 > INT_MAX || gridb > INT_MAX) return SV_ERR_TOO_LARGE;
     // vector loads need 16-byte aligned rows: in the row stage of the logits,
     // in the draw of the logits and the draft probabilities (8 elements)
     const bool vec = aligned(target_logits, 16) && ((size_t)vocab * lsz) % 16 == 0;
@@ -2272,6 +2319,8 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     p.cd = cd;
     p.ex = kExp2Coef;
     p.len = greedy ? 1.0 : (double)lenience;
+    p.rows_grid = (int)grid1;
+    p.help_polls = kHelpPolls;
     p.polls_slot = extras && extras->wait_polls > 0 ? extras->wait_polls : kSlotPolls;
     p.drop_slot = extras && extras->withhold_partial > 0 ? extras->withhold_partial - 1 : -1;
     p.err_count = extras ? extras->error_count : nullptr;
@@ -2288,7 +2337,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
         ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)grid1, batch, p, s, ev_mid)
                                      : launch_greedy_t<SV_FP32>(vec, (int)grid1, batch, p, s, ev_mid);
     } else {
-        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)grid1, (int)grid2, p, s, ev_mid,
+        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)gridh, helpers ? batch : (int)grid2, p, s, ev_mid,
                            extras ? (hipEvent_t)extras->ev_tele : nullptr);
     }
     if (!ok) return SV_ERR_LAUNCH;

@@ -43,7 +43,7 @@ def walltime_improvement(alpha: float, gamma: int, c: float) -> float:
     return tokens / (gamma * c + 1.0)
 
 
-def optimal_gamma(alpha: float, c: float, gamma_max: int = 62) -> int:
+def optimal_gamma(alpha: float, c: float, gamma_max: int = 63) -> int:
     """The gamma in 1..gamma_max with the largest walltime improvement,
     found by evaluating every candidate (the page's recipe); ties go to the
     smaller gamma.  alpha in [0, 1], c >= 0."""

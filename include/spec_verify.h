@@ -50,8 +50,10 @@ extern "C" {
 #define SV_SAMPLE 0 /* temperature sampling, exact rejection rule            */
 #define SV_GREEDY 1 /* argmax standardisation; T, draft_probs, uniforms unused */
 
-/* Largest supported gamma (one bit per draft position in a 64-bit word). */
-#define SV_MAX_GAMMA 62
+/* Largest supported gamma: the gamma + 1 rows of a sequence are the bits of
+ * a 64-bit word (the reject mask uses bits 0 .. gamma-1 and keeps bit 63 for
+ * an invalid draft token). */
+#define SV_MAX_GAMMA 63
 
 /* Status codes returned synchronously by every entry point. */
 #define SV_OK 0

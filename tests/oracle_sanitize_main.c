@@ -4,7 +4,7 @@
  * UndefinedBehaviorSanitizer into a standalone program that includes the
  * oracle's source, then run on the CPU.  It calls every entry point of the
  * oracle over seeded random shapes and inputs with the awkward cases in them
- * (vocabularies of 1, 2 and 3 entries, gamma up to 62, -inf logits, zero
+ * (vocabularies of 1, 2 and 3 entries, gamma up to 63, -inf logits, zero
  * draft probabilities, out-of-range draft tokens, uniforms of 0 and 1,
  * lenience 0 and 1, top-k with k above V, nucleus at 1), every output and
  * auxiliary array allocated to its exact size so that any access past an end
@@ -174,7 +174,7 @@ int main(void)
     int failures = 0;
     for (int trial = 0; trial < 60; ++trial) {
         const int V = vocabs[below(8)];
-        const int gamma = trial == 0 ? 62 : 1 + below(8);
+        const int gamma = trial == 0 ? 63 : 1 + below(8);
         const int B = 1 + below(6);
         const int zd = below(2) ? REF_BF16 : REF_FP32;
         const int qd = below(2) ? REF_BF16 : REF_FP32;

@@ -15,6 +15,7 @@ import scipy.stats
 
 import oracle
 from oracle import analysis
+import exact_rejection_sampling_temp_amd as sv
 from exact_rejection_sampling_temp_amd import driver
 from tests import synth
 from tests.laws import target_law
@@ -63,7 +64,7 @@ def test_optimal_gamma_is_the_argmax_of_theorem_3_8():
     for a in np.linspace(0.05, 0.95, 19):
         prev = None
         for c in (0.0, 0.01, 0.02, 0.05, 0.1, 0.2, 0.5):
-            vals = [analysis.walltime_improvement(a, g, c) for g in range(1, 63)]
+            vals = [analysis.walltime_improvement(a, g, c) for g in range(1, sv.SV_MAX_GAMMA + 1)]
             want = int(np.argmax(vals)) + 1
             got = driver.optimal_gamma(a, c)
             assert got == want, (a, c, got, want)

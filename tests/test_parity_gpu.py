@@ -86,7 +86,7 @@ def test_unaligned_vocab_scalar_path(V):
     _check(synth.make_inputs("c2", 500 + V, B=6, V=V))
 
 
-@pytest.mark.parametrize("gamma", [1, 2, 16, 62])
+@pytest.mark.parametrize("gamma", [1, 2, 16, 62, 63])
 def test_gamma_extremes(gamma):
     _check(synth.make_inputs("c4", 600 + gamma, B=4, gamma=gamma, V=3000))
 

@@ -33,7 +33,7 @@ def test_fp32_sample(V):
     _check(synth.make_inputs("c2", 900 + V, B=64, V=V))
 
 
-@pytest.mark.parametrize("gamma", [1, 16, 62])
+@pytest.mark.parametrize("gamma", [1, 16, 62, 63])
 @pytest.mark.parametrize("V", [8, 100, 512])
 def test_bf16_sample(gamma, V):
     _check(synth.make_inputs("c5", 1000 + gamma * 7 + V, B=32, gamma=gamma, V=V))
