@@ -61,6 +61,7 @@ class Extras(ctypes.Structure):
         ("error_count", ctypes.c_void_p),
         ("withhold_partial", ctypes.c_int32),
         ("wait_polls", ctypes.c_int32),
+        ("help_polls", ctypes.c_int32),
     ]
 
 
@@ -186,7 +187,7 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
                 mode: str | int = "sample", *, n_accepted=None, out_tokens=None, workspace=None,
                 aux: dict | None = None, events=None, stream=None, lenience: float = 1.0,
                 error_count=None, _test_withhold_partial: int = 0, _test_wait_polls: int = 0,
-                _noalloc: bool = False):
+                _test_help_polls: int = 0, _noalloc: bool = False):
     """Batched verify-and-sample on the GPU.
 
     target_logits [B, gamma+1, V] fp32/bf16, draft_probs [B, gamma, V] fp32/bf16
@@ -205,7 +206,8 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     ``error_count``: optional uint32 device counter (one element, zeroed by
     the caller) of sequences whose outputs were withheld because a bounded
     device-side wait ran out (n_accepted = -2).  ``_test_withhold_partial``,
-    ``_test_wait_polls``: sv_extras_t's test hooks for that failure path.
+    ``_test_wait_polls``: sv_extras_t's test hooks for that failure path;
+    ``_test_help_polls``: its hook bounding the draw helpers' wait.
     """
     import torch
     lib = load_library()
@@ -250,12 +252,13 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
     ex = None
     if error_count is not None:
         _check_out(error_count, torch.int32, 1, dev, "error_count")
-    if aux or events or error_count is not None or _test_withhold_partial or _test_wait_polls:
+    if aux or events or error_count is not None or _test_withhold_partial or _test_wait_polls or _test_help_polls:
         ex = Extras()
         if error_count is not None:
             ex.error_count = error_count.data_ptr()
         ex.withhold_partial = int(_test_withhold_partial)
         ex.wait_polls = int(_test_wait_polls)
+        ex.help_polls = int(_test_help_polls)
         for k, t in (aux or {}).items():
             setattr(ex, k, t.data_ptr())
         if events:

@@ -68,6 +68,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr uint64_t kInvalidBit = 1ull << 63;
+// A ready-list entry: (b + 1) | n << kReadyNShift, so that whoever reads a
+// sequence's entry learns its n in the same load (sample mode limits B to
+// kMaxListed).
+constexpr int kReadyNShift = 26;
+constexpr uint32_t kReadySeqMask = (1u << kReadyNShift) - 1u;
+constexpr int kMaxListed = (int)kReadySeqMask - 1;
 // SeqCtl::pad[0], bit k: the merge of row k ran out of its bounded wait for a
 // partial (the sequence's outputs are withheld if k is on its walk, k <= n)
 constexpr double kResidEps = 1e-15;  // [ST] correction_distribution
@@ -116,7 +122,7 @@ struct SubSum {
     double E;   // sum of e_v = exp((z_v - m)/T)
     double EA;  // sum of e_v over A = {v : e_v > q_v S_row} (residual support)
     double QA;  // sum of q_v over A
-    double pad;
+    double done;  // nonzero once a first-launch draw helper has written the three sums
 };
 static_assert(sizeof(SubSum) == 32, "SubSum layout");
 
@@ -125,8 +131,8 @@ struct SeqCtl {
     uint64_t mask;    // bit k: position k rejected; kInvalidBit: a bad draft token
     uint64_t dec;     // bit k: position k decided (a rejection also sets every
                       // later bit); bit gamma: row gamma's statistics out
-    uint64_t claim;   // draw chunks claimed in the first launch, in order: chunks
-                      // 0 .. claim-1 (claims past nch2 take nothing)
+    uint64_t claim;   // telemetry calls: draw chunks claimed before the last launch,
+                      // in order: chunks 0 .. claim-1 (claims past nch2 take nothing)
     uint64_t cnt2;    // draw wave tasks finished in the second launch
     uint64_t retire;  // low word: users done in the second launch; high word:
                       // the sequence's rank in the ready list
@@ -630,7 +636,7 @@ struct Params {
     uint64_t* part1;  // [rows][nch1][2]
     RowStat* stats;   // [rows]
     SubSum* sub;      // [B][nsub] sums of the sub-chunks (kSubW elements) of row n
-    uint32_t* ready;  // [B] 1 + the sequences, in the order their n became known
+    uint32_t* ready;  // [B] the sequences, in the order their n became known (ready-list entries)
     uint32_t* ready_cnt;
     int32_t* n_out;
     int32_t* tok_out;
@@ -656,6 +662,9 @@ struct Params {
                        // partial, so that the merge's bounded wait runs out
     uint32_t* err_count;  // optional: sequences whose merge wait ran out
 };
+
+__device__ __forceinline__ int ready_seq(uint32_t e) { return (int)(e & kReadySeqMask) - 1; }
+__device__ __forceinline__ int ready_n(uint32_t e) { return (int)(e >> kReadyNShift); }
 
 // bits 0 .. gamma (one per row of a sequence)
 __device__ __forceinline__ uint64_t rows_mask(int gamma) { return (2ull << gamma) - 1ull; }
@@ -817,7 +826,7 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_
             uint64_t* slot = reinterpret_cast<uint64_t*>(p.sub + (size_t)b * p.nsub + sidx);
             dep ^= xchg_agent(slot, dbits(E)) ^ xchg_agent(slot + 1, dbits(EA)) ^ xchg_agent(slot + 2, dbits(QA));
         } else {
-            p.sub[(size_t)b * p.nsub + sidx] = SubSum{E, EA, QA, 0.0};
+            p.sub[(size_t)b * p.nsub + sidx] = SubSum{E, EA, QA, 1.0};
         }
     }
     if constexpr (COUNTED) {
@@ -1125,42 +1134,35 @@ __device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint6
 // ------------------------------------------------------------ sample, launch 1
 
 // Draw helpers, appended to the first launch's grid after every row block:
-// helper j serves the sequence whose n became known (j / nch2)-th.  It waits,
-// bounded, until that sequence is in the ready list, then claims one of its
-// draw chunks and computes the chunk's sums.  Being dispatched after every
-// row block, the helpers take no slot from the rows of any position, and they
-// wait only on row blocks, which never wait on them.  A helper whose wait runs
-// out leaves its chunk to the last launch.
+// helper j computes draw chunk j % nch2 of the sequence whose n became known
+// (j / nch2)-th.  It waits, bounded, until that sequence is in the ready
+// list; the entry carries b and n, and the sequence's reject bits and row n's
+// statistics were published before it.  Being dispatched after every row
+// block, the helpers take no slot from the rows of any position, and they
+// wait only on row blocks, which never wait on them.  A helper whose wait
+// runs out leaves its chunk to the last launch, which finds it by the sums'
+// done marks.
 template <int DT, int PT, bool VEC2>
 __device__ void help_draw(const Params& p, int j)
 {
-    __shared__ int sm_hb, sm_hc;
-    __shared__ uint64_t sm_hm;
+    __shared__ uint32_t sm_he;
     const int r = j / p.nch2;
     if (threadIdx.x == 0) {
-        int hb = -1, hc = -1;
+        uint32_t e = 0;
         for (int it = 0; it < p.help_polls; ++it) {
-            const uint32_t e = ld_agent32(&p.ready[r]);
-            if (e != 0u) {
-                hb = (int)e - 1;
-                break;
-            }
+            e = ld_agent32(&p.ready[r]);
+            if (e != 0u) break;
             __builtin_amdgcn_s_sleep(8);
         }
-        if (hb >= 0 && hb < p.B) {
-            const uint32_t cl = (uint32_t)add_agent64(&p.ctl[hb].claim, 1ull);
-            if (cl < (uint32_t)p.nch2) {
-                hc = (int)cl;
-                // read once the sequence is listed: every reject bit up to n,
-                // and row n's statistics, were published before it was
-                sm_hm = ld_agent(&p.ctl[hb].mask + (cl & p.zero));
-            }
-        }
-        sm_hb = hb;
-        sm_hc = hc;
+        sm_he = e;
     }
     __syncthreads();
-    if (sm_hc >= 0) draw_chunk<DT, PT, VEC2, false>(p, sm_hb, sm_hc, sm_hm);
+    const uint32_t e = sm_he;
+    const int b = ready_seq(e), n = ready_n(e);
+    if (e == 0u || b >= p.B || n > p.gamma) return;
+    // (a mask with n's reject bit alone: the draw's row and residual follow from n)
+    const uint64_t mask = n < p.gamma ? 1ull << n : 0ull;
+    draw_chunk<DT, PT, VEC2, false>(p, b, j - r * p.nch2, mask);
 }
 
 // Decision inputs read through the scalar cache: every lane of the workgroup
@@ -1405,10 +1407,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
         const uint64_t decbits = maskbits ? (all & ~((1ull << k) - 1ull)) : (1ull << k);
         const uint64_t old = or_agent(&p.ctl[b].dec, decbits | (uint64_t)(fold64(dd) & p.zero));
         if ((old & all) != all && ((old | decbits) & all) == all) {
-            // n of this sequence just became known: record the order (read
-            // by the second launch)
+            // n of this sequence just became known: record the order, with n
+            // (read by the draw helpers and the last launch).  Every position
+            // before k was decided and accepted (a rejection there would have
+            // set bit k already), so a rejection here makes n = k, and the
+            // bonus row's block completing the mask makes n = gamma.  Else
+            // n > k is the first reject bit of the mask, read once dec has
+            // returned: that rejection was performed before its decision
+            // bits, which this block saw.
+            int n = maskbits ? k : p.gamma;
+            if (!maskbits && k < p.gamma)
+                n = first_reject(ld_agent(&p.ctl[b].mask + (fold64(old) & p.zero)), p.gamma);
             const uint32_t slot = add_agent(p.ready_cnt, 1u);
-            __hip_atomic_store(&p.ready[slot], (uint32_t)b + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t e = ((uint32_t)b + 1u) | ((uint32_t)n << kReadyNShift);
+            __hip_atomic_store(&p.ready[slot], e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             or_agent(&p.ctl[b].retire, (uint64_t)slot << 32);
         }
     }
@@ -1521,8 +1533,8 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
     // (every sequence is in the list once launch 1 is done, and leaves it when
     // the last of its users here clears its workspace)
     const uint32_t listed = ld_agent32(&p.ready[r]);
-    const int b = (int)listed - 1;
-    if (b < 0 || b >= p.B) return;
+    const int b = ready_seq(listed);
+    if (listed == 0u || b >= p.B) return;
     // the first launch's claim count, final during this launch -- unless the
     // sequence has been cleared meanwhile, in which case it is no longer
     // listed and this workgroup had nothing to do
@@ -1546,24 +1558,46 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
 
 // The last launch when the first launch carries draw helpers: one workgroup
 // per sequence, the sequence resolved last first.  It computes the draw
-// chunks no helper took (chunks L1 .. nch2-1, L1 the claim count), runs the
-// draw and clears the sequence.
+// sub-chunks no helper did (their done mark is 0), runs the draw and clears
+// the sequence.  The first launch is over, so plain loads see its writes.
 template <int DT, int PT, bool VEC2>
 __global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
 {
+    __shared__ int sm_left;
     const int r = p.B - 1 - (int)blockIdx.x;
-    const int b = (int)p.ready[r] - 1;
-    if (b < 0 || b >= p.B) return;  // (every sequence is in the list once launch 1 is done)
-    // the first launch is over: its claim count and the reject mask are final
-    const int l1 = (int)min((uint32_t)p.ctl[b].claim, (uint32_t)p.nch2);
-    const int left = p.nch2 - l1;
+    const uint32_t e = p.ready[r];
+    const int b = ready_seq(e);
+    if (e == 0u || b >= p.B) return;  // (every sequence is in the list once launch 1 is done)
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const uint64_t mask = p.ctl[b].mask;
-    bool fin_wave = left == 0 && threadIdx.x < 64;  // nothing left: wave 0 draws
-    for (int c2 = l1; c2 < p.nch2; ++c2)
-        if (draw_chunk<DT, PT, VEC2, true>(p, b, c2, mask, (uint64_t)kWaves * left)) fin_wave = true;
+    const SubSum* ss = p.sub + (size_t)b * p.nsub;
+    // sub-chunks left: wave w looks at w, w + 4, ... (lane i at the i-th of them)
+    if (threadIdx.x == 0) sm_left = 0;
+    __syncthreads();
+    int mine = 0;
+    for (int s0 = w; s0 < p.nsub; s0 += kWaves * 64) {
+        const int sidx = s0 + kWaves * lane;
+        mine += __popcll(__ballot(sidx < p.nsub && ss[sidx].done == 0.0));
+    }
+    if (lane == 0 && mine) atomicAdd(&sm_left, mine);
+    __syncthreads();
+    const int left = sm_left;
+    bool fin_wave = left == 0 && w == 0;  // nothing left: wave 0 draws
+    if (left > 0) {
+        for (int s0 = w; s0 < p.nsub; s0 += kWaves * 64) {
+            const int sidx = s0 + kWaves * lane;
+            uint64_t todo = __ballot(sidx < p.nsub && ss[sidx].done == 0.0);
+            while (todo) {
+                const int i = __builtin_ctzll(todo);
+                todo &= todo - 1ull;
+                if (draw_wave<DT, PT, VEC2, true>(p, b, (s0 + kWaves * i) * kSubPerWave, mask, (uint64_t)left))
+                    fin_wave = true;
+            }
+        }
+    }
     if (fin_wave) finish_wave<DT, PT, VEC2>(p, b);
     __syncthreads();  // the draw's reads are done
-    if (threadIdx.x < 64) cleanup_wave(p, b, (uint32_t)r, true);
+    if (w == 0) cleanup_wave(p, b, (uint32_t)r, true);
 }
 
 // ----------------------------------------------------------------- greedy mode
@@ -2266,6 +2300,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     const bool helpers = !greedy && !tele;
     const long long gridh = helpers ? grid1 + (long long)batch * L.nch2 : grid1;
     if (nch1 > 0xffff || gridh > INT_MAX || grid2 > INT_MAX || gridb > INT_MAX) return SV_ERR_TOO_LARGE;
+    if (!greedy && batch > kMaxListed) return SV_ERR_TOO_LARGE;
     // vector loads need 16-byte aligned rows: in the row stage of the logits,
     // in the draw of the logits and the draft probabilities (8 elements)
     const bool vec = aligned(target_logits, 16) && ((size_t)vocab * lsz) % 16 == 0;
@@ -2320,7 +2355,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     p.ex = kExp2Coef;
     p.len = greedy ? 1.0 : (double)lenience;
     p.rows_grid = (int)grid1;
-    p.help_polls = kHelpPolls;
+    p.help_polls = extras && extras->help_polls > 0 ? extras->help_polls : kHelpPolls;
     p.polls_slot = extras && extras->wait_polls > 0 ? extras->wait_polls : kSlotPolls;
     p.drop_slot = extras && extras->withhold_partial > 0 ? extras->withhold_partial - 1 : -1;
     p.err_count = extras ? extras->error_count : nullptr;

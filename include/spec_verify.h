@@ -67,7 +67,8 @@ extern "C" {
 #define SV_ERR_WORKSPACE -8     /* workspace NULL or smaller than sv_workspace_bytes */
 #define SV_ERR_ALIGNMENT -9     /* a pointer is not aligned to its element size, or
                                    the workspace is not 256-byte aligned             */
-#define SV_ERR_TOO_LARGE -10    /* the problem exceeds the launch-grid limits        */
+#define SV_ERR_TOO_LARGE -10    /* the problem exceeds the launch-grid limits, or
+                                   batch > 67 108 861 in sample mode               */
 #define SV_ERR_LAUNCH -11       /* the HIP runtime rejected a kernel launch          */
 #define SV_ERR_LENIENCE -12     /* sample mode with lenience outside [0, 1]          */
 #define SV_ERR_STANDARDIZE -13  /* unknown method, k < 1, or top_p outside (0, 1]    */
@@ -130,6 +131,12 @@ typedef struct {
      * failed while every kernel still completes normally. */
     int32_t withhold_partial;
     int32_t wait_polls;
+    /* Test of the draw's fallback only; leave 0.  help_polls > 0 bounds the
+     * wait of the first launch's draw helpers for their sequence to that
+     * many polls (sample mode, vocab > 512, no telemetry); a helper whose
+     * wait runs out leaves its draw chunk to the last launch.  The results
+     * are the same for any value. */
+    int32_t help_polls;
 } sv_extras_t;
 
 /* sizeof(sv_extras_t) as this library was built: a binding that mirrors

@@ -53,6 +53,26 @@ def test_merge_wait_that_runs_out_withholds_the_outputs(position):
     compare({"n_accepted": n2, "out_tokens": out2}, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
 
 
+@pytest.mark.parametrize("cfg,B,V,polls", [("c4", 12, 40_000, 1), ("c3", 16, 30_001, 1), ("c4", 256, 152_064, 1),
+                                           ("c5", 32, 256_000, 1), ("c4", 64, 152_064, 64)])
+def test_draw_chunks_the_helpers_leave_to_the_last_launch(cfg, B, V, polls):
+    """The first launch's draw helpers wait for their sequence at most
+    `polls` polls here, so that most of them give up and the last launch
+    computes their chunks (all of them for the small grids, a mix for the
+    large ones).  The outputs are the oracle's, and the workspace is left
+    zero."""
+    import torch
+    import exact_rejection_sampling_temp_amd as sv
+    d = synth.make_inputs(cfg, 1320 + B, B=B, V=V)
+    print(f"[helpers] {cfg} B={d['B']} gamma={d['gamma']} V={d['V']} polls={polls}", flush=True)
+    x = to_device(d)
+    r = run_ref(d)
+    n, out = _call(d, x, _test_help_polls=polls)
+    compare({"n_accepted": n, "out_tokens": out}, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
+    for ws in sv._ws_cache.values():
+        assert int(ws.count_nonzero()) == 0
+
+
 def test_calls_on_another_stream():
     import torch
     import exact_rejection_sampling_temp_amd as sv
