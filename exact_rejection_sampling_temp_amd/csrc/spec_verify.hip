@@ -850,22 +850,27 @@ __device__ __forceinline__ double draw_weight(const Params& p, bool use_resid, f
 }
 
 // Clears everything the call left in the workspace for sequence b.  Run by
-// one wave, by the sequence's last user.
-// Run by one wave, by the sequence's last user.  `listed`: the sequence is
-// in the ready list (sample mode), at `rank`.  It leaves the list first: a
-// second-launch workgroup that reads the control words and then still finds
-// the sequence listed has read them before they were cleared, since every
-// clearing store is issued only once the exchange has returned (its value
-// feeds their addresses).
-__device__ void cleanup_wave(const Params& p, int b, uint32_t rank, bool listed)
+// one wave, by the sequence's last user.  `listed`: the sequence is in the
+// ready list (sample mode), at `rank`.  With `exchange` it leaves the list
+// first: a second-launch workgroup that reads the control words and then
+// still finds the sequence listed has read them before they were cleared,
+// since every clearing store is issued only once the exchange has returned
+// (its value feeds their addresses).  Without it (no other workgroup reads
+// the sequence's workspace any more) the list entry is simply cleared.
+__device__ void cleanup_wave(const Params& p, int b, uint32_t rank, bool listed, bool exchange = true)
 {
     const int lane = threadIdx.x & 63;
     const int G1 = p.gamma + 1;
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
     uint32_t d = 0;
     if (listed && lane == 0) {
-        d = __hip_atomic_exchange(&p.ready[rank], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (rank == 0) d ^= __hip_atomic_exchange(p.ready_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (exchange) {
+            d = __hip_atomic_exchange(&p.ready[rank], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (rank == 0) d ^= __hip_atomic_exchange(p.ready_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            p.ready[rank] = 0u;
+            if (rank == 0) *p.ready_cnt = 0u;
+        }
     }
     const size_t dz = __builtin_amdgcn_readfirstlane(d) & p.zero;
     if (lane < 4) reinterpret_cast<uint4*>(p.ctl + b + dz)[lane] = z4;
@@ -899,8 +904,10 @@ __device__ __forceinline__ void retire_wave(const Params& p, int b, uint32_t use
 // sub-chunk sums; a scan over the sub-chunk weights in index order finds the
 // sub-chunk holding u * total, and a scan of its elements, a 512-element
 // group at a time with every weight recomputed exactly, finds the token.
-template <int DT, int PT, bool VEC2>
-__device__ void finish_wave(const Params& p, int b)
+// MARKS: the sums come from the first launch's draw helpers, each with its
+// done mark; if a mark is missing the wave writes nothing and returns false.
+template <int DT, int PT, bool VEC2, bool MARKS>
+__device__ bool finish_wave(const Params& p, int b)
 {
     const int lane = threadIdx.x & 63;
     const int G1 = p.gamma + 1;
@@ -913,10 +920,12 @@ __device__ void finish_wave(const Params& p, int b)
         if (lane < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + lane];
     }
     const uint64_t mask = ld_agent(&p.ctl[b].mask);
+    const uint64_t merge_lost = ld_agent(&p.ctl[b].pad[0]);
     const double ug = (double)p.uniforms[(int64_t)b * G1 + p.gamma];
     const SubSum* ss = p.sub + (size_t)b * p.nsub;
     const int nrounds = (p.nsub + kRound - 1) / kRound;
     double rE[kRPL], rEA[kRPL], rQA[kRPL];
+    bool marked = true;  // (MARKS) every sub-chunk of the rounds loaded so far has its done mark
     auto load_round = [&](int r) {
 #pragma unroll
         for (int i = 0; i < kRPL; ++i) {
@@ -925,18 +934,22 @@ __device__ void finish_wave(const Params& p, int b)
                 rE[i] = ld_agent_d(&ss[j].E);
                 rEA[i] = ld_agent_d(&ss[j].EA);
                 rQA[i] = ld_agent_d(&ss[j].QA);
+                if constexpr (MARKS) marked = marked && ss[j].done != 0.0;
             } else {
                 rE[i] = rEA[i] = rQA[i] = 0.0;
             }
         }
     };
     load_round(0);
+    if constexpr (MARKS) {
+        if (__ballot(!marked) != 0) return false;
+    }
 
     const bool bad = __ballot(lane < p.gamma && (tok < 0 || tok >= p.V)) != 0;
     const int n = first_reject(mask, p.gamma);
     // a row on the walk whose merge ran out of its wait: the sequence is
     // reported like an invalid one, with n = -2, and counted
-    const bool failed = (ld_agent(&p.ctl[b].pad[0]) & ((2ull << n) - 1ull)) != 0;
+    const bool failed = (merge_lost & ((2ull << n) - 1ull)) != 0;
     const bool invalid = (mask & kInvalidBit) || bad || failed;
     const bool resid = n < p.gamma;
     int t = -1;
@@ -945,7 +958,12 @@ __device__ void finish_wave(const Params& p, int b)
         // exact normaliser of row n and the residual mass
         double a = 0.0;
         for (int r = 0; r < nrounds; ++r) {
-            if (r > 0) load_round(r);
+            if (r > 0) {
+                load_round(r);
+                if constexpr (MARKS) {
+                    if (__ballot(!marked) != 0) return false;  // (no output written yet)
+                }
+            }
 #pragma unroll
             for (int i = 0; i < kRPL; ++i) a += rE[i];
         }
@@ -1119,6 +1137,7 @@ __device__ void finish_wave(const Params& p, int b)
         p.n_out[b] = failed ? -2 : invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = (!invalid && resid) ? Z : NAN;
     }
+    return true;
 }
 
 // One claimed draw chunk of sequence b, by the whole workgroup: wave w takes
@@ -1549,41 +1568,48 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
     if (left == 0) fin_wave = threadIdx.x < 64;  // nothing left: workgroup 0 draws
     else if (draw_chunk<DT, PT, VEC2, true>(p, b, l1 + j, mask, (uint64_t)kWaves * left)) fin_wave = true;
     if (fin_wave) {
-        finish_wave<DT, PT, VEC2>(p, b);
+        finish_wave<DT, PT, VEC2, false>(p, b);
         retire_wave(p, b, (uint32_t)users + 1u);
     }
     __syncthreads();  // this workgroup's work is done
     if (threadIdx.x < 64) retire_wave(p, b, (uint32_t)users + 1u);
 }
 
-// The last launch when the first launch carries draw helpers: one workgroup
-// per sequence, the sequence resolved last first.  It computes the draw
-// sub-chunks no helper did (their done mark is 0), runs the draw and clears
-// the sequence.  The first launch is over, so plain loads see its writes.
+// The last launch when the first launch carries draw helpers: workgroup b
+// finishes sequence b.  Wave 0 runs the draw from the helpers' sums; should a
+// sub-chunk lack its done mark (its helper's wait ran out), the workgroup
+// computes every unmarked sub-chunk, counting them out, and the wave that
+// completes the count runs the draw.  Then the sequence is cleared.  The
+// first launch is over, so plain loads see its writes, and no other
+// workgroup reads this sequence's workspace.
 template <int DT, int PT, bool VEC2>
 __global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
 {
-    __shared__ int sm_left;
-    const int r = p.B - 1 - (int)blockIdx.x;
-    const uint32_t e = p.ready[r];
-    const int b = ready_seq(e);
-    if (e == 0u || b >= p.B) return;  // (every sequence is in the list once launch 1 is done)
+    __shared__ int sm_ok, sm_left;
+    const int b = (int)blockIdx.x;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint64_t mask = p.ctl[b].mask;
-    const SubSum* ss = p.sub + (size_t)b * p.nsub;
-    // sub-chunks left: wave w looks at w, w + 4, ... (lane i at the i-th of them)
+    const uint64_t all = rows_mask(p.gamma);
+    if ((p.ctl[b].dec & all) != all) return;  // (every sequence is decided in the first launch)
+    const uint32_t rank = (uint32_t)(p.ctl[b].retire >> 32);  // its place in the ready list
+    if (w == 0) {
+        const bool ok = finish_wave<DT, PT, VEC2, true>(p, b);
+        if (lane == 0) sm_ok = ok ? 1 : 0;
+    }
     if (threadIdx.x == 0) sm_left = 0;
     __syncthreads();
-    int mine = 0;
-    for (int s0 = w; s0 < p.nsub; s0 += kWaves * 64) {
-        const int sidx = s0 + kWaves * lane;
-        mine += __popcll(__ballot(sidx < p.nsub && ss[sidx].done == 0.0));
-    }
-    if (lane == 0 && mine) atomicAdd(&sm_left, mine);
-    __syncthreads();
-    const int left = sm_left;
-    bool fin_wave = left == 0 && w == 0;  // nothing left: wave 0 draws
-    if (left > 0) {
+    if (!sm_ok) {
+        const uint64_t mask = p.ctl[b].mask;
+        const SubSum* ss = p.sub + (size_t)b * p.nsub;
+        // sub-chunks left: wave w looks at w, w + 4, ... (lane i at the i-th of them)
+        int mine = 0;
+        for (int s0 = w; s0 < p.nsub; s0 += kWaves * 64) {
+            const int sidx = s0 + kWaves * lane;
+            mine += __popcll(__ballot(sidx < p.nsub && ss[sidx].done == 0.0));
+        }
+        if (lane == 0 && mine) atomicAdd(&sm_left, mine);
+        __syncthreads();
+        const int left = sm_left;
+        bool fin_wave = false;
         for (int s0 = w; s0 < p.nsub; s0 += kWaves * 64) {
             const int sidx = s0 + kWaves * lane;
             uint64_t todo = __ballot(sidx < p.nsub && ss[sidx].done == 0.0);
@@ -1594,10 +1620,10 @@ __global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
                     fin_wave = true;
             }
         }
+        if (fin_wave) finish_wave<DT, PT, VEC2, false>(p, b);
     }
-    if (fin_wave) finish_wave<DT, PT, VEC2>(p, b);
     __syncthreads();  // the draw's reads are done
-    if (w == 0) cleanup_wave(p, b, (uint32_t)r, true);
+    if (w == 0) cleanup_wave(p, b, rank, true, false);
 }
 
 // ----------------------------------------------------------------- greedy mode
