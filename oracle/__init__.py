@@ -61,6 +61,7 @@ class _Aux(ctypes.Structure):
         ("n_flags", ctypes.c_void_p),
         ("beta", ctypes.c_void_p),
         ("alpha", ctypes.c_void_p),
+        ("p_out", ctypes.c_void_p),
     ]
 
 
@@ -151,6 +152,7 @@ def spec_verify_ref(target_logits: np.ndarray, draft_probs: np.ndarray | None,
             "flag_pos": np.empty(B, np.int32),
             "n_decisions": np.empty(B, np.int32),
             "n_flags": np.empty(B, np.int32),
+            "p_out": np.empty(B, np.float64),
         }
         if telemetry:
             arrs["beta"] = np.empty((B, G), np.float64)

@@ -90,6 +90,8 @@ typedef struct {
     int32_t* n_flags;     /* [B]          near-boundary decisions taken                        */
     double*  beta;        /* [B][gamma]   sum_v min(p_i, q_i) for EVERY position (sample mode) */
     double*  alpha;       /* [gamma]      mean over the batch of beta[.][i]                    */
+    double*  p_out;       /* [B]          p_n(t), t the token drawn at position n (the bonus token
+                                          when n = gamma), sample mode; NaN otherwise              */
 } ref_aux_t;
 
 /* Exact promotion of one input element to double: fp32 directly, bf16 by
@@ -239,6 +241,8 @@ static void verify_sample_one(int b, int gamma, int V,
     tok_out[n] = t;
     for (int i = n + 1; i <= gamma; ++i) tok_out[i] = -1;
     *n_out = n;
+    /* p still holds p_n, the row the token was drawn for */
+    if (aux && aux->p_out) aux->p_out[b] = p[t];
     if (aux && aux->flag_pos) aux->flag_pos[b] = first_flag;
     if (aux && aux->n_decisions) aux->n_decisions[b] = n_dec;
     if (aux && aux->n_flags) aux->n_flags[b] = n_flag;
@@ -322,6 +326,7 @@ int spec_verify_ref(int batch, int gamma, int vocab,
         fill_nan(aux->row_sum, B * G1);
         fill_nan(aux->beta, B * G);
         fill_nan(aux->alpha, G);
+        fill_nan(aux->p_out, B);
     }
 
 #ifdef _OPENMP

@@ -111,6 +111,7 @@ static int run_verify(int B, int gamma, int V, int zd, int qd, float T, float le
         aux.flag_pos = (int32_t*)xmalloc(sizeof(int32_t) * (size_t)B);
         aux.n_decisions = (int32_t*)xmalloc(sizeof(int32_t) * (size_t)B);
         aux.n_flags = (int32_t*)xmalloc(sizeof(int32_t) * (size_t)B);
+        aux.p_out = (double*)xmalloc(sizeof(double) * (size_t)B);
     }
     if (with_tele) {
         aux.beta = (double*)xmalloc(sizeof(double) * (size_t)B * gamma);
@@ -138,6 +139,7 @@ static int run_verify(int B, int gamma, int V, int zd, int qd, float T, float le
     free(aux.n_flags);
     free(aux.beta);
     free(aux.alpha);
+    free(aux.p_out);
     if (bad) fprintf(stderr, "spec_verify_ref: rc %d on B=%d gamma=%d V=%d\n", rc, B, gamma, V);
     return bad;
 }

@@ -456,6 +456,41 @@ def test_invalid_draft_token_marks_sequence():
         assert r["n_accepted"][b] >= 0
 
 
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_p_out_is_the_target_probability_of_the_drawn_token(name):
+    """p_out[b] is p_n(t) for the token t drawn at position n, the bonus
+    token's p_gamma(t) when every draft passed ([FI] "Speculative Sampling:
+    The Core Algorithm", Phase 4): pinned to scipy's softmax of row n at the
+    temperature, over seeded batches with rejections, full acceptances (q
+    equal to p), the residual fallback's rows and invalid drafts."""
+    d = synth.make_inputs(name, 21, B=24, V=3000)
+    z, q, x, u = d["target_logits"], d["draft_probs"].copy(), d["draft_tokens"].copy(), d["uniforms"]
+    T = d["temperature"]
+    bf16 = z.dtype == np.uint16
+    z64 = (synth.bf16_bits_to_f32(z) if bf16 else z).astype(np.float64)
+    B, G1, V = z.shape
+    G = G1 - 1
+    # sequences 0..3: q = p at every position, so every draft passes (bonus draws)
+    for b in range(4):
+        for i in range(G):
+            pi = scipy.special.softmax(z64[b, i] / np.float64(np.float32(T)))
+            qi = pi.astype(np.float32)
+            q[b, i] = qi if q.dtype != np.uint16 else synth.f32_to_bf16_bits(qi)
+            x[b, i] = int(np.argmax(pi))
+    x[5, 1] = V  # an invalid draft
+    r = oracle.spec_verify_ref(z, q, x, u, T)
+    n, out = r["n_accepted"], r["out_tokens"]
+    assert np.any(n == G) and np.any((n >= 0) & (n < G))
+    for b in range(B):
+        if n[b] < 0:
+            assert np.isnan(r["p_out"][b])
+            continue
+        ref = scipy.special.softmax(z64[b, n[b]] / np.float64(np.float32(T)))
+        np.testing.assert_allclose(r["p_out"][b], ref[out[b, n[b]]], rtol=1e-12, atol=1e-300)
+    g = oracle.spec_verify_ref(z, None, x, None, 1.0, oracle.GREEDY)
+    assert np.all(np.isnan(g["p_out"]))
+
+
 def test_argument_validation():
     z = np.zeros((1, 2, 4), np.float32)
     q = np.full((1, 1, 4), 0.25, np.float32)
