@@ -52,6 +52,7 @@ class Extras(ctypes.Structure):
         ("resid_mass", ctypes.c_void_p),
         ("row_max", ctypes.c_void_p),
         ("row_sum", ctypes.c_void_p),
+        ("p_out", ctypes.c_void_p),
         ("ev_begin", ctypes.c_void_p),
         ("ev_mid", ctypes.c_void_p),
         ("ev_end", ctypes.c_void_p),
@@ -165,6 +166,7 @@ def _workspace(device, nbytes: int, stream):
 
 
 _AUX_SPEC = {"p_tok": ("float64", "BG"), "q_tok": ("float64", "BG"), "resid_mass": ("float64", "B"),
+             "p_out": ("float64", "B"),
              "row_max": ("float32", "BG1"), "row_sum": ("float64", "BG1"),
              "beta": ("float64", "BG"), "alpha": ("float64", "G")}
 
@@ -197,7 +199,8 @@ def spec_verify(target_logits, draft_probs, draft_tokens, uniforms, temperature:
 
     ``aux``: optional dict of preallocated device tensors with keys among
     p_tok [B,gamma] f64, q_tok [B,gamma] f64, resid_mass [B] f64,
-    row_max [B,gamma+1] f32, row_sum [B,gamma+1] f64, and the acceptance-rate
+    row_max [B,gamma+1] f32, row_sum [B,gamma+1] f64, p_out [B] f64 (p_n of the
+    drawn token), and the acceptance-rate
     telemetry beta [B,gamma] f64 / alpha [gamma] f64 (sample mode; either one
     makes the call stream every row, see include/spec_verify.h).
     ``events``: optional (begin, mid, end) or (begin, mid, end, tele) raw

@@ -643,6 +643,7 @@ struct Params {
     double* aux_p;
     double* aux_q;
     double* aux_resid;
+    double* aux_pout;  // [B] p_n(t) of the drawn token
     float* aux_rmax;
     double* aux_rsum;
     int B, gamma, V, nch1, nch2, nsub, probs_dtype;
@@ -839,6 +840,14 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_
     return false;
 }
 
+// Element i of a row of logits or probabilities, as float.
+template <int DT>
+__device__ __forceinline__ float elem_at(const void* row, int64_t i)
+{
+    if constexpr (DT == SV_BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(row)[i] << 16);
+    else return static_cast<const float*>(row)[i];
+}
+
 // Weight of one element of row n for the inverse-CDF draw: max(0, p - l q)
 // with p = e / S and l the lenience (1: the exact method), or e itself for
 // the bonus / fallback draw.
@@ -954,6 +963,7 @@ __device__ bool finish_wave(const Params& p, int b)
     const bool resid = n < p.gamma;
     int t = -1;
     double Z = NAN;
+    double pout = NAN;  // p_n(t), when asked for
     if (!invalid) {
         // exact normaliser of row n and the residual mass
         double a = 0.0;
@@ -1114,6 +1124,8 @@ __device__ bool finish_wave(const Params& p, int b)
             // row n itself, which always has an element with e_v = 1)
             if (t < 0) t = scan_back(p.nsub * kSubPerWave - 1, false);
         }
+        // p_n(t) = e_t / S, e_t by the draw's arithmetic
+        if (p.aux_pout && t >= 0) pout = draw_weight(p, false, elem_at<DT>(zrow, t), 0.0f, nMcd, invS) * invS;
     }
 
     // outputs and telemetry
@@ -1136,6 +1148,7 @@ __device__ bool finish_wave(const Params& p, int b)
         if (failed && p.err_count) add_agent(p.err_count, 1u);
         p.n_out[b] = failed ? -2 : invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = (!invalid && resid) ? Z : NAN;
+        if (p.aux_pout) p.aux_pout[b] = pout;
     }
     return true;
 }
@@ -1756,6 +1769,7 @@ __global__ __launch_bounds__(kThreads) void k_draw_greedy(const Params p)
     if (lane == 0) {
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = NAN;
+        if (p.aux_pout) p.aux_pout[b] = NAN;
     }
     cleanup_wave(p, b, 0u, false);  // (no ready list in greedy mode)
 }
@@ -1779,13 +1793,6 @@ __global__ void k_fill_zero(uint4* p, size_t n16, unsigned char* tail, size_t nt
 // chunk on a few entries.  Telemetry calls take that path.
 constexpr int kSmallK = 8;              // entries per lane
 constexpr int kSmallV = 64 * kSmallK;   // 512
-
-template <int DT>
-__device__ __forceinline__ float elem_at(const void* row, int64_t i)
-{
-    if constexpr (DT == SV_BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(row)[i] << 16);
-    else return static_cast<const float*>(row)[i];
-}
 
 // max / min over the wave with DPP moves and four row read-outs (see
 // wave_sum_dpp)
@@ -1835,7 +1842,7 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
     float st_m = NAN;
     double st_S = NAN, st_P = NAN, st_Q = NAN;
     int n = p.gamma, t = -1;
-    double Z = NAN;
+    double Z = NAN, pout = NAN;
     if (!invalid) {
         float z[kSmallK];
         double e[kSmallK];
@@ -1941,6 +1948,14 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
                 t = wave_max_i(last);
             }
             if (!resid) Z = NAN;
+            // p_n(t) = e_t / S: e and S of row n are in registers
+            if (p.aux_pout && t >= 0) {
+                double et = 0.0;
+#pragma unroll
+                for (int j = 0; j < kSmallK; ++j)
+                    if (j == t / 64) et = e[j];
+                pout = __shfl(et, t % 64, 64) * invS;
+            }
         }
     }
 
@@ -1962,6 +1977,7 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
     if (lane == 0) {
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = invalid || GREEDY ? NAN : Z;
+        if (p.aux_pout) p.aux_pout[b] = invalid || GREEDY ? NAN : pout;
     }
 }
 
@@ -2021,7 +2037,7 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
     float st_m = NAN;
     double st_S = NAN, st_P = NAN, st_Q = NAN;
     int n = p.gamma, t = -1;
-    double Z = NAN;
+    double Z = NAN, pout = NAN;
     bool active = live && !invalid;  // this row's walk goes on
     double e = 0.0, S = 0.0;
     float z = -INFINITY;
@@ -2091,6 +2107,9 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
         const uint32_t pr = (uint32_t)((pos >> (16 * r)) & 0xffffull);
         if (walked) t = hr ? __builtin_ctz(hr) : (pr ? 31 - __builtin_clz(pr) : -1);
         if (walked && resid) Z = Zr;
+        // p_n(t) = e_t / S: lane t of this row holds e_t
+        const double et = __shfl(e, base + (t & 15), 64);
+        if (walked && t >= 0) pout = et / S;
     }
 
     if (live && l < G1) {
@@ -2111,6 +2130,7 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
     if (live && l == 0) {
         p.n_out[b] = invalid ? -1 : n;
         if (p.aux_resid) p.aux_resid[b] = invalid || GREEDY ? NAN : Z;
+        if (p.aux_pout) p.aux_pout[b] = invalid || GREEDY ? NAN : pout;
     }
 }
 
@@ -2360,6 +2380,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     p.aux_p = extras ? extras->p_tok : nullptr;
     p.aux_q = extras ? extras->q_tok : nullptr;
     p.aux_resid = extras ? extras->resid_mass : nullptr;
+    p.aux_pout = extras ? extras->p_out : nullptr;
     p.aux_rmax = extras ? extras->row_max : nullptr;
     p.aux_rsum = extras ? extras->row_sum : nullptr;
     p.aux_beta = tele ? extras->beta : nullptr;

@@ -92,6 +92,9 @@ typedef struct {
     float*  row_max;    /* [B][gamma+1] max_v z of each row the walk normalised
                                         (sample) or examined (greedy)            */
     double* row_sum;    /* [B][gamma+1] sum_v exp((z - row_max) / T), sample mode */
+    double* p_out;      /* [B]          p_n(t): the target probability, at T, of the
+                                        token t drawn at position n (the bonus
+                                        token when n = gamma), sample mode      */
     /* hipEvent_t handles recorded on `stream`: before the first launch,
      * after the first launch (the row stage, which in sample mode also
      * streams most of the draw), and after the last launch.  Any may be

@@ -42,6 +42,7 @@ def run_gpu(d: dict, mode: str = "sample", with_aux: bool = True, dev_inputs=Non
             "resid_mass": torch.empty(B, dtype=torch.float64, device=dv),
             "row_max": torch.empty((B, G1), dtype=torch.float32, device=dv),
             "row_sum": torch.empty((B, G1), dtype=torch.float64, device=dv),
+            "p_out": torch.empty(B, dtype=torch.float64, device=dv),
         }
     if telemetry:
         dv = x["target_logits"].device
@@ -140,5 +141,13 @@ def check_aux(gpu: dict, ref: dict, rtol_p: float):
     np.testing.assert_allclose(gpu["row_sum"][rows], ref["row_sum"][rows], rtol=rtol_p)
     same = valid & (gpu["n_accepted"] == ref["n_accepted"]) & (ref["n_accepted"] < G)
     np.testing.assert_allclose(gpu["resid_mass"][same], ref["resid_mass"][same], rtol=1e-9, atol=1e-15)
+    # p_n of the drawn token, where both sides drew the same token at the same n
+    if "p_out" in gpu:
+        nn = np.clip(ref["n_accepted"], 0, G)
+        rows_b = np.arange(B)
+        drew = valid & (gpu["n_accepted"] == ref["n_accepted"]) & \
+            (gpu["out_tokens"][rows_b, nn] == ref["out_tokens"][rows_b, nn])
+        np.testing.assert_allclose(gpu["p_out"][drew], ref["p_out"][drew], rtol=1e-9, atol=1e-300)
+        assert np.all(np.isnan(gpu["p_out"][gpu["n_accepted"] < 0]))
     # positions past the walk are NaN on the GPU side
     assert np.all(np.isnan(gpu["p_tok"][~sel & valid[:, None]]))

@@ -96,6 +96,17 @@ def test_greedy_reduced():
         _check(synth.make_inputs("c3", 700 + seed, B=16, V=40_000), mode="greedy")
 
 
+@pytest.mark.parametrize("V", [40_000, 300, 12])
+def test_greedy_leaves_p_out_nan(V):
+    # p_out is a sample-mode output: greedy calls (the many-workgroup path,
+    # one wave per sequence, four sequences per wave) write NaN
+    d = synth.make_inputs("c3", 720 + V, B=6, gamma=4 if V > 16 else 3, V=V)
+    g = run_gpu(d, "greedy", with_aux=True)
+    r = run_ref(d, "greedy")
+    compare(g, r, d["gamma"], draft_tokens=d["draft_tokens"], vocab=d["V"])
+    assert np.all(np.isnan(g["p_out"]))
+
+
 def test_greedy_ties_pick_lowest_index():
     rng = np.random.default_rng(71)
     B, gamma, V = 64, 4, 9000

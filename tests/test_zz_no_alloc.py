@@ -15,7 +15,7 @@ from tests.gpu_util import compare, run_ref, to_device
 pytestmark = pytest.mark.gpu
 
 _AUX = (("p_tok", "float64", "BG"), ("q_tok", "float64", "BG"), ("resid_mass", "float64", "B"),
-        ("row_max", "float32", "BG1"), ("row_sum", "float64", "BG1"))
+        ("row_max", "float32", "BG1"), ("row_sum", "float64", "BG1"), ("p_out", "float64", "B"))
 
 
 def _aux(B, gamma, dev):
