@@ -153,6 +153,18 @@ def test_bf16_long_tie_runs(method, kw):
     _check(synth.f32_to_bf16_bits(z), method, **kw)
 
 
+@pytest.mark.parametrize("method,kw", [("topk", dict(k=50)), ("topk", dict(k=120_000)), ("topp", dict(top_p=0.9)),
+                                       ("topp", dict(top_p=0.5, T=0.7))])
+@pytest.mark.parametrize("V", [155_648, 155_656, 200_000])
+def test_bf16_rows_at_and_past_the_register_path(method, kw, V):
+    """bf16 rows whose every wave run just fits in registers (V = 155 648)
+    and rows one group longer or much longer (read twice), with ties."""
+    rng = np.random.default_rng(15)
+    z = (rng.standard_normal((3, V)) * 3).astype(np.float32)
+    z[1] = np.round(z[1], 1)
+    _check(synth.f32_to_bf16_bits(z), method, **kw)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_degenerate_rows(dt):
     """Rows of -inf only, a single finite entry among -inf, half -inf,
