@@ -22,16 +22,19 @@
 //      Phase 3: the walk stops at the first rejection), so a workgroup that
 //      finds an earlier position of its sequence rejected skips its chunk;
 //      with position-major launch order most unneeded rows are never read.
-//      From a middle position on, once every position up to the first
-//      rejection n is decided, such a workgroup works on the draw of its
-//      sequence instead: it claims one draw chunk of row n (the residual
-//      max(0, p_n - q_n), or p_gamma when n = gamma) and computes its fp64
-//      sums, so the draw of most sequences overlaps the row work of others.
+//      The decider that completes a sequence's decisions appends it, with
+//      its n, to a ready list.  After every row workgroup the grid holds
+//      B * nch2 draw helpers: helper j waits (bounded) for the (j / nch2)-th
+//      sequence of the ready list and computes the fp64 sums of draw chunk
+//      j % nch2 of its row n (the residual max(0, p_n - q_n), or p_gamma
+//      when n = gamma), so the draws of the sequences resolved first overlap
+//      the rows of the others.
 //
-//   2. k_rest_sample.  Workgroups claim the draw chunks the first launch
-//      left, the sequences resolved last first; the wave that completes a
-//      sequence's sums turns them into the inverse-CDF draw and writes the
-//      outputs, and the sequence's last user clears its workspace.
+//   2. k_finish_sample, one workgroup per sequence: it computes any draw
+//      chunk no helper did, turns the sums into the inverse-CDF draw, writes
+//      the outputs and clears the sequence's workspace.  (Calls that ask for
+//      the acceptance telemetry stream every row and sweep the rows between
+//      the launches; their last launch is k_rest_sample.)
 //
 // Greedy mode is k_rows_greedy (same grid; chunk argmax) and k_draw_greedy.
 //
@@ -41,11 +44,13 @@
 // (e_v, normaliser, residual, prefix sums), so its token boundaries agree
 // with an fp64 evaluation to rounding level.
 //
-// Cross-workgroup data (row partials, row statistics, draw sums) are
-// written with device-scope atomic exchanges whose returned values feed the
-// operand of the atomic that announces them (an arrival counter or a
-// decision bit), so they are complete device-wide before anyone can learn
-// of them; readers use device-scope atomic loads.
+// Cross-workgroup data within a launch (row statistics, and the draw sums
+// of k_rest_sample) are written with device-scope atomic exchanges whose
+// returned values feed the operand of the atomic that announces them (a
+// decision bit, a completion count), so they are complete device-wide
+// before anyone can learn of them; readers use device-scope atomic loads.
+// Row partials go out with device-scope stores whose words are never zero,
+// and the row's last workgroup polls each slot until both have landed.
 //
 // Workspace: per-sequence control words and per-row arrival counters, then
 // scratch for partials, row statistics and draw sums.  It must be all zero
