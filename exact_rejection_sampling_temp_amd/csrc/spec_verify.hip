@@ -672,6 +672,46 @@ struct Params {
 __device__ __forceinline__ int ready_seq(uint32_t e) { return (int)(e & kReadySeqMask) - 1; }
 __device__ __forceinline__ int ready_n(uint32_t e) { return (int)(e >> kReadyNShift); }
 
+// Which part of the work a workgroup takes, from its index.  Host and
+// device: the kernels decode their blocks with these, and a CPU test checks
+// them against the launch geometry and the workspace layout.
+struct RowBlock {
+    int k, b, c;  // position, sequence, chunk of the row stage
+};
+__host__ __device__ __forceinline__ RowBlock row_block(uint32_t bid, int nch1, int B)
+{
+    const uint32_t t = bid / (uint32_t)nch1;  // k * B + b
+    return RowBlock{(int)(t / (uint32_t)B), (int)(t % (uint32_t)B), (int)(bid % (uint32_t)nch1)};
+}
+struct DrawTask {
+    int r, c2;  // rank in the ready list, draw chunk
+};
+__host__ __device__ __forceinline__ DrawTask helper_task(int j, int nch2)
+{
+    const int r = j / nch2;
+    return DrawTask{r, j - r * nch2};
+}
+// the sub-chunk (kSubW elements, one wave task) of wave w of draw chunk c2
+__host__ __device__ __forceinline__ int wave_sub(int c2, int w) { return c2 * kWaves + w; }
+struct BetaBlock {
+    int b, i, c;  // sequence, position, telemetry chunk
+};
+__host__ __device__ __forceinline__ BetaBlock beta_block(uint32_t bid, int nchb, int gamma)
+{
+    const int t = (int)(bid / (uint32_t)nchb);  // b * gamma + i
+    const int b = t / gamma;
+    return BetaBlock{b, t - b * gamma, (int)(bid % (uint32_t)nchb)};
+}
+struct RestTask {
+    int r, j;  // rank in the ready list, the sequence's workgroup
+};
+__host__ __device__ __forceinline__ RestTask rest_task(int i, int B, int nch2)
+{
+    const int per = nch2 - 1 > 1 ? nch2 - 1 : 1;
+    if (i < B) return RestTask{B - 1 - i, 0};
+    return RestTask{B - 1 - (i - B) / per, 1 + (i - B) % per};
+}
+
 // bits 0 .. gamma (one per row of a sequence)
 __device__ __forceinline__ uint64_t rows_mask(int gamma) { return (2ull << gamma) - 1ull; }
 // n from a reject mask: the first rejected position, gamma if none
@@ -1164,8 +1204,7 @@ __device__ bool finish_wave(const Params& p, int b)
 template <int DT, int PT, bool VEC2, bool COUNTED>
 __device__ __forceinline__ bool draw_chunk(const Params& p, int b, int c2, uint64_t mask, uint64_t target = 0)
 {
-    const int w = threadIdx.x >> 6;
-    return draw_wave<DT, PT, VEC2, COUNTED>(p, b, c2 * kSubPerChunk + w * kSubPerWave, mask, target);
+    return draw_wave<DT, PT, VEC2, COUNTED>(p, b, wave_sub(c2, threadIdx.x >> 6) * kSubPerWave, mask, target);
 }
 
 // ------------------------------------------------------------ sample, launch 1
@@ -1183,7 +1222,8 @@ template <int DT, int PT, bool VEC2>
 __device__ void help_draw(const Params& p, int j)
 {
     __shared__ uint32_t sm_he;
-    const int r = j / p.nch2;
+    const DrawTask task = helper_task(j, p.nch2);
+    const int r = task.r;
     if (threadIdx.x == 0) {
         uint32_t e = 0;
         for (int it = 0; it < p.help_polls; ++it) {
@@ -1199,7 +1239,7 @@ __device__ void help_draw(const Params& p, int j)
     if (e == 0u || b >= p.B || n > p.gamma) return;
     // (a mask with n's reject bit alone: the draw's row and residual follow from n)
     const uint64_t mask = n < p.gamma ? 1ull << n : 0ull;
-    draw_chunk<DT, PT, VEC2, false>(p, b, j - r * p.nch2, mask);
+    draw_chunk<DT, PT, VEC2, false>(p, b, task.c2, mask);
 }
 
 // Decision inputs read through the scalar cache: every lane of the workgroup
@@ -1262,10 +1302,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
         help_draw<DT, PT, VEC2>(p, (int)(blockIdx.x - (unsigned)p.rows_grid));
         return;
     }
-    const int c = (int)(blockIdx.x % (unsigned)p.nch1);
-    const int t = (int)(blockIdx.x / (unsigned)p.nch1);
-    const int b = t % p.B;
-    const int k = t / p.B;
+    const RowBlock rb = row_block(blockIdx.x, p.nch1, p.B);
+    const int c = rb.c, b = rb.b, k = rb.k;
     const int G1 = p.gamma + 1;
     const int64_t row = (int64_t)b * G1 + k;
 
@@ -1476,10 +1514,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_num_sgpr(kMainSgprs
 template <int DT, int PT, bool VEC2>
 __global__ __launch_bounds__(kThreads) void k_beta(const Params p)
 {
-    const int c = (int)(blockIdx.x % (unsigned)p.nchb);
-    const int t = (int)(blockIdx.x / (unsigned)p.nchb);  // b * gamma + i
-    const int b = t / p.gamma;
-    const int i = t - b * p.gamma;
+    const BetaBlock bb = beta_block(blockIdx.x, p.nchb, p.gamma);
+    const int c = bb.c, b = bb.b, i = bb.i;
+    const int t = b * p.gamma + i;
     const int64_t row = (int64_t)b * (p.gamma + 1) + i;
     __shared__ double sm_d[kWaves];
     const int tid = (int)threadIdx.x;
@@ -1563,10 +1600,8 @@ __global__ __launch_bounds__(kThreads) void k_beta_merge(const Params p)
 template <int DT, int PT, bool VEC2>
 __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
 {
-    const int i = (int)blockIdx.x;
-    const int per = max(p.nch2 - 1, 1);
-    const int r = p.B - 1 - (i < p.B ? i : (i - p.B) / per);
-    const int j = i < p.B ? 0 : 1 + (i - p.B) % per;
+    const RestTask rt = rest_task((int)blockIdx.x, p.B, p.nch2);
+    const int r = rt.r, j = rt.j;
     // (every sequence is in the list once launch 1 is done, and leaves it when
     // the last of its users here clears its workspace)
     const uint32_t listed = ld_agent32(&p.ready[r]);
@@ -1664,10 +1699,8 @@ __global__ __launch_bounds__(kThreads) void k_rows_greedy(const Params p)
     constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
     constexpr int W = DT == SV_BF16 ? 8 : 4;
     constexpr int CH = EPT * kThreads;
-    const int c = (int)(blockIdx.x % (unsigned)p.nch1);
-    const int t = (int)(blockIdx.x / (unsigned)p.nch1);
-    const int b = t % p.B;
-    const int k = t / p.B;
+    const RowBlock rb = row_block(blockIdx.x, p.nch1, p.B);
+    const int c = rb.c, b = rb.b, k = rb.k;
     const int G1 = p.gamma + 1;
     const int64_t row = (int64_t)b * G1 + k;
 
@@ -2140,26 +2173,24 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
 }
 
 template <int DT, int PT>
-bool launch_small_t(bool greedy, const Params& p, hipStream_t s)
+bool launch_small_t(bool greedy, bool tiny, int grid, const Params& p, hipStream_t s)
 {
-    if (p.V <= kTinyV && p.gamma < 16) {
-        const dim3 grid((unsigned)((p.B + 4 * kWaves - 1) / (4 * kWaves)));  // four sequences per wave
-        if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_tiny<DT, PT, false>), grid, dim3(kThreads), 0, s, p);
+    if (tiny) {  // four sequences per wave
+        if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_tiny<DT, PT, false>), dim3(grid), dim3(kThreads), 0, s, p);
         return hipGetLastError() == hipSuccess;
     }
-    const dim3 grid((unsigned)((p.B + kWaves - 1) / kWaves));
-    if (greedy) hipLaunchKernelGGL((k_small<DT, DT, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_small<DT, PT, false>), grid, dim3(kThreads), 0, s, p);
+    if (greedy) hipLaunchKernelGGL((k_small<DT, DT, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_small<DT, PT, false>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError() == hipSuccess;
 }
 
-bool launch_small(int dt, int pt, bool greedy, const Params& p, hipStream_t s)
+bool launch_small(int dt, int pt, bool greedy, bool tiny, int grid, const Params& p, hipStream_t s)
 {
-    if (dt == SV_FP32 && (greedy || pt == SV_FP32)) return launch_small_t<SV_FP32, SV_FP32>(greedy, p, s);
-    if (dt == SV_FP32) return launch_small_t<SV_FP32, SV_BF16>(greedy, p, s);
-    if (greedy || pt == SV_FP32) return launch_small_t<SV_BF16, SV_FP32>(greedy, p, s);
-    return launch_small_t<SV_BF16, SV_BF16>(greedy, p, s);
+    if (dt == SV_FP32 && (greedy || pt == SV_FP32)) return launch_small_t<SV_FP32, SV_FP32>(greedy, tiny, grid, p, s);
+    if (dt == SV_FP32) return launch_small_t<SV_FP32, SV_BF16>(greedy, tiny, grid, p, s);
+    if (greedy || pt == SV_FP32) return launch_small_t<SV_BF16, SV_FP32>(greedy, tiny, grid, p, s);
+    return launch_small_t<SV_BF16, SV_BF16>(greedy, tiny, grid, p, s);
 }
 
 // ---------------------------------------------------------------- host dispatch
@@ -2216,6 +2247,43 @@ bool launch_greedy_t(bool vec, int grid1, int B, const Params& p, hipStream_t s,
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The launch geometry of one verify call: which kernels run on how many
+// workgroups.  status is SV_ERR_TOO_LARGE when a grid would pass the limits
+// (a grid's block count as int, nch1 within the 16 bits of a row counter,
+// the batch within what a ready-list entry holds).
+struct Plan {
+    int nch1;          // row-stage chunks per row
+    long long grid1;   // row-stage workgroups (G1 * B * nch1)
+    long long gridh;   // first launch: the row stage, then B * nch2 draw helpers (sample, no telemetry)
+    long long grid2;   // last launch: B (greedy, or with helpers) or B * nch2 (telemetry)
+    long long gridb;   // telemetry sweep: B * gamma * nchb
+    bool small;        // V <= 512 without telemetry: one launch of k_small or k_tiny
+    bool tiny;         //   k_tiny: V <= 16 and gamma < 16
+    long long grid_small;
+    bool helpers;
+    int status;
+};
+
+Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, bool tele)
+{
+    const Layout L = make_layout(batch, gamma, vocab);
+    Plan q{};
+    const int chunk1 = logits_dtype == SV_BF16 ? kChunkBf16 : kChunkFp32;
+    q.nch1 = (vocab + chunk1 - 1) / chunk1;
+    q.grid1 = (long long)(gamma + 1) * batch * q.nch1;
+    q.helpers = !greedy && !tele;
+    q.gridh = q.helpers ? q.grid1 + (long long)batch * L.nch2 : q.grid1;
+    q.grid2 = greedy || q.helpers ? (long long)batch : (long long)batch * L.nch2;
+    q.gridb = tele ? (long long)batch * gamma * L.nchb : 0;
+    q.small = vocab <= kSmallV && !tele;
+    q.tiny = q.small && vocab <= kTinyV && gamma < 16;
+    q.grid_small = q.tiny ? ((long long)batch + 4 * kWaves - 1) / (4 * kWaves) : ((long long)batch + kWaves - 1) / kWaves;
+    q.status = SV_OK;
+    if (q.nch1 > 0xffff || q.gridh > INT_MAX || q.grid2 > INT_MAX || q.gridb > INT_MAX) q.status = SV_ERR_TOO_LARGE;
+    if (!greedy && batch > kMaxListed) q.status = SV_ERR_TOO_LARGE;
+    return q;
+}
 
 // The checks of every verify entry point that need no workspace and no HIP
 // call; SV_OK or the status to return.
@@ -2339,19 +2407,12 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     if (!workspace || workspace_bytes < L.total) return SV_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SV_ERR_ALIGNMENT;
 
-    const int G1 = gamma + 1;
-    const int chunk1 = logits_dtype == SV_BF16 ? kChunkBf16 : kChunkFp32;
-    const int nch1 = (vocab + chunk1 - 1) / chunk1;
-    const long long grid1 = (long long)G1 * batch * nch1;
-    const long long grid2 = greedy ? (long long)batch : (long long)batch * L.nch2;
     const bool tele = !greedy && extras && (extras->beta || extras->alpha);
-    const long long gridb = tele ? (long long)batch * gamma * L.nchb : 0;
     // sample mode without telemetry: draw helpers follow the row blocks of
     // the first launch, and the last launch is one workgroup per sequence
-    const bool helpers = !greedy && !tele;
-    const long long gridh = helpers ? grid1 + (long long)batch * L.nch2 : grid1;
-    if (nch1 > 0xffff || gridh > INT_MAX || grid2 > INT_MAX || gridb > INT_MAX) return SV_ERR_TOO_LARGE;
-    if (!greedy && batch > kMaxListed) return SV_ERR_TOO_LARGE;
+    const Plan q = make_plan(batch, gamma, vocab, logits_dtype, greedy, tele);
+    if (q.status != SV_OK) return q.status;
+    const int nch1 = q.nch1;
     // vector loads need 16-byte aligned rows: in the row stage of the logits,
     // in the draw of the logits and the draft probabilities (8 elements)
     const bool vec = aligned(target_logits, 16) && ((size_t)vocab * lsz) % 16 == 0;
@@ -2406,7 +2467,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     p.cd = cd;
     p.ex = kExp2Coef;
     p.len = greedy ? 1.0 : (double)lenience;
-    p.rows_grid = (int)grid1;
+    p.rows_grid = (int)q.grid1;
     p.help_polls = extras && extras->help_polls > 0 ? extras->help_polls : kHelpPolls;
     p.polls_slot = extras && extras->wait_polls > 0 ? extras->wait_polls : kSlotPolls;
     p.drop_slot = extras && extras->withhold_partial > 0 ? extras->withhold_partial - 1 : -1;
@@ -2416,15 +2477,15 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     if (extras && extras->ev_begin && hipEventRecord((hipEvent_t)extras->ev_begin, s) != hipSuccess)
         return SV_ERR_LAUNCH;
     bool ok;
-    if (vocab <= kSmallV && !tele) {
+    if (q.small) {
         // one launch, one wave per sequence (the workspace is not touched)
-        ok = launch_small(logits_dtype, probs_dtype, greedy, p, s);
+        ok = launch_small(logits_dtype, probs_dtype, greedy, q.tiny, (int)q.grid_small, p, s);
         if (ok && ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) ok = false;
     } else if (greedy) {
-        ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)grid1, batch, p, s, ev_mid)
-                                     : launch_greedy_t<SV_FP32>(vec, (int)grid1, batch, p, s, ev_mid);
+        ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)q.grid1, batch, p, s, ev_mid)
+                                     : launch_greedy_t<SV_FP32>(vec, (int)q.grid1, batch, p, s, ev_mid);
     } else {
-        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)gridh, helpers ? batch : (int)grid2, p, s, ev_mid,
+        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)q.gridh, (int)q.grid2, p, s, ev_mid,
                            extras ? (hipEvent_t)extras->ev_tele : nullptr);
     }
     if (!ok) return SV_ERR_LAUNCH;
