@@ -2055,7 +2055,7 @@ __device__ __forceinline__ double row_incl_scan16(double v)
     return v + dpp_d<0x118>(v);
 }
 
-template <int DT, int PT, bool GREEDY>
+template <int DT, int PT, bool GREEDY, int TG>
 __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
 {
     const int lane = threadIdx.x & 63;
@@ -2069,8 +2069,23 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
     float ul = 0.0f;
     if (live && l < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + l];
     if (!GREEDY && live && l < G1) ul = p.uniforms[(int64_t)b * G1 + l];
+    // every target row of the sequence (gamma + 1 <= TG) in registers,
+    // loaded in one round trip with the tokens and uniforms: zs[i] = z_i(l)
+    float zs[TG];
+#pragma unroll
+    for (int i = 0; i < TG; ++i) {
+        zs[i] = -INFINITY;
+        if (i <= p.gamma && live && l < V)
+            zs[i] = elem_at<DT>(static_cast<const char*>(p.logits) +
+                                    (size_t)((int64_t)b * G1 + i) * V * (DT == SV_BF16 ? 2 : 4), l);
+    }
     const uint64_t bad = __ballot(live && l < p.gamma && (tok < 0 || tok >= V));
     const bool invalid = ((bad >> (16 * r)) & 0xffffull) != 0ull;
+    // lane i of a row: q_i(x_i), gathered once the tokens are in
+    float qx = 0.0f;
+    if (!GREEDY && live && !invalid && l < p.gamma)
+        qx = elem_at<PT>(static_cast<const char*>(p.probs) + (size_t)((int64_t)b * p.gamma + l) * V * (PT == SV_BF16 ? 2 : 4),
+                         tok);
 
     float st_m = NAN;
     double st_S = NAN, st_P = NAN, st_Q = NAN;
@@ -2079,10 +2094,10 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
     bool active = live && !invalid;  // this row's walk goes on
     double e = 0.0, S = 0.0;
     float z = -INFINITY;
+#pragma unroll 1
     for (int i = 0; i <= p.gamma; ++i) {
         if (__ballot(active) == 0ull) break;
-        const void* zrow = static_cast<const char*>(p.logits) + (size_t)((int64_t)b * G1 + i) * V * (DT == SV_BF16 ? 2 : 4);
-        z = active && l < V ? elem_at<DT>(zrow, l) : -INFINITY;
+        z = active && l < V ? zs[i] : -INFINITY;  // (i is uniform: the arrays stay in registers)
         const float m = row_max16(z);
         if (active && l == i) st_m = m;
         if constexpr (GREEDY) {
@@ -2101,17 +2116,18 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
             if (active && l == i) st_S = Si;
             if (i == p.gamma) break;  // the rows still walking accepted every draft
             const int x = __shfl(tok, base + i, 64);
-            const float zx = __shfl(z, base + (x & 15), 64);  // (x < V <= 16 on an active row)
+            const double ex = __shfl(ei, base + (x & 15), 64);  // e_x: lane x of the row holds it (x < V <= 16)
             const float ui = __shfl(ul, base + i, 64);
             double P = 0.0, Q = 0.0;
             bool rej = false;
+            const float qi = __shfl(qx, base + i, 64);  // q_i(x_i)
             if (active) {
-                P = zx > -INFINITY ? exp2(((double)zx - (double)m) * p.cd) / Si : 0.0;
-                const void* qrow = static_cast<const char*>(p.probs) +
-                                   (size_t)((int64_t)b * p.gamma + i) * V * (PT == SV_BF16 ? 2 : 4);
-                Q = (double)elem_at<PT>(qrow, x);
-                const double thr = Q <= 0.0 ? 1.0 : fmin(1.0, P / (p.len * Q));
-                rej = !((double)ui <= thr);
+                P = ex * (1.0 / Si);
+                Q = (double)qi;
+                // u <= min(1, p / (l q)), q <= 0 accepting, without the
+                // divisions: for u <= 1 the same as q <= 0 or u l q <= p
+                // (rounding can differ only within the flagged window)
+                rej = !((double)ui <= 1.0 && (Q <= 0.0 || (double)ui * (p.len * Q) <= P));
             }
             if (active && l == i) { st_P = P; st_Q = Q; }
             if (active && rej) {
@@ -2176,8 +2192,14 @@ template <int DT, int PT>
 bool launch_small_t(bool greedy, bool tiny, int grid, const Params& p, hipStream_t s)
 {
     if (tiny) {  // four sequences per wave
-        if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_tiny<DT, PT, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        // (the rows of a sequence held in registers: 8 when gamma + 1 <= 8, else 16)
+        if (p.gamma + 1 <= 8) {
+            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_tiny<DT, PT, false, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+        } else {
+            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, kTinyV>), dim3(grid), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_tiny<DT, PT, false, kTinyV>), dim3(grid), dim3(kThreads), 0, s, p);
+        }
         return hipGetLastError() == hipSuccess;
     }
     if (greedy) hipLaunchKernelGGL((k_small<DT, DT, true>), dim3(grid), dim3(kThreads), 0, s, p);
