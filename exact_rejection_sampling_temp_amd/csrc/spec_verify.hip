@@ -2026,45 +2026,67 @@ __global__ __launch_bounds__(kThreads) void k_small(const Params p)
 // every lane active, each row masked once its walk has ended.
 constexpr int kTinyV = 16;
 
-__device__ __forceinline__ float row_max16(float v)
+// Reductions and scans inside rows of RL = 8 or 16 lanes: quad swaps, the
+// half-row mirror (8 lanes), the row mirror (16); row_shr for the scan, with
+// the shifts that would cross an 8-lane segment masked off.
+template <int RL>
+__device__ __forceinline__ float row_max(float v)
 {
     v = fmaxf(v, dpp_f<0xB1>(v));
     v = fmaxf(v, dpp_f<0x4E>(v));
     v = fmaxf(v, dpp_f<0x141>(v));
-    return fmaxf(v, dpp_f<0x140>(v));
+    if constexpr (RL == 16) v = fmaxf(v, dpp_f<0x140>(v));
+    return v;
 }
-__device__ __forceinline__ int row_min16(int v)
+template <int RL>
+__device__ __forceinline__ int row_min(int v)
 {
     v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
     v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
     v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false));
-    return min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));
+    if constexpr (RL == 16) v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));
+    return v;
 }
-__device__ __forceinline__ double row_sum16(double v)
+template <int RL>
+__device__ __forceinline__ double row_sum(double v)
 {
     v += dpp_d<0xB1>(v);
     v += dpp_d<0x4E>(v);
     v += dpp_d<0x141>(v);
-    return v + dpp_d<0x140>(v);
+    if constexpr (RL == 16) v += dpp_d<0x140>(v);
+    return v;
 }
-__device__ __forceinline__ double row_incl_scan16(double v)
+template <int RL>
+__device__ __forceinline__ double row_incl_scan(double v)
 {
-    v += dpp_d<0x111>(v);
-    v += dpp_d<0x112>(v);
-    v += dpp_d<0x114>(v);
-    return v + dpp_d<0x118>(v);
+    if constexpr (RL == 16) {
+        v += dpp_d<0x111>(v);
+        v += dpp_d<0x112>(v);
+        v += dpp_d<0x114>(v);
+        return v + dpp_d<0x118>(v);
+    } else {
+        const int l = (int)threadIdx.x & 7;
+        double t = dpp_d<0x111>(v);
+        v += l >= 1 ? t : 0.0;
+        t = dpp_d<0x112>(v);
+        v += l >= 2 ? t : 0.0;
+        t = dpp_d<0x114>(v);
+        return v + (l >= 4 ? t : 0.0);
+    }
 }
 
-template <int DT, int PT, bool GREEDY, int TG>
+template <int DT, int PT, bool GREEDY, int TG, int RL>
 __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
 {
+    constexpr int RPW = 64 / RL;  // rows (sequences) per wave
     const int lane = threadIdx.x & 63;
-    const int r = lane >> 4, l = lane & 15;  // row (sequence) of the wave, lane in the row
-    const int b = (int)((blockIdx.x * kWaves + (threadIdx.x >> 6)) * 4) + r;
+    const int r = lane / RL, l = lane % RL;  // row (sequence) of the wave, lane in the row
+    const int b = (int)((blockIdx.x * kWaves + (threadIdx.x >> 6)) * RPW) + r;
     const bool live = b < p.B;  // rows past the batch run along masked (no loads, no stores)
     const int G1 = p.gamma + 1;
     const int V = p.V;
-    const int base = lane & ~15;
+    const int base = lane & ~(RL - 1);
+    constexpr uint64_t kRowBits = RL == 16 ? 0xffffull : 0xffull;
     int32_t tok = 0;
     float ul = 0.0f;
     if (live && l < p.gamma) tok = p.tokens[(int64_t)b * p.gamma + l];
@@ -2080,7 +2102,7 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
                                     (size_t)((int64_t)b * G1 + i) * V * (DT == SV_BF16 ? 2 : 4), l);
     }
     const uint64_t bad = __ballot(live && l < p.gamma && (tok < 0 || tok >= V));
-    const bool invalid = ((bad >> (16 * r)) & 0xffffull) != 0ull;
+    const bool invalid = ((bad >> (RL * r)) & kRowBits) != 0ull;
     // lane i of a row: q_i(x_i), gathered once the tokens are in
     float qx = 0.0f;
     if (!GREEDY && live && !invalid && l < p.gamma)
@@ -2098,10 +2120,10 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
     for (int i = 0; i <= p.gamma; ++i) {
         if (__ballot(active) == 0ull) break;
         z = active && l < V ? zs[i] : -INFINITY;  // (i is uniform: the arrays stay in registers)
-        const float m = row_max16(z);
+        const float m = row_max<RL>(z);
         if (active && l == i) st_m = m;
         if constexpr (GREEDY) {
-            const int a = row_min16(l < V && z == m ? l : INT_MAX);
+            const int a = row_min<RL>(l < V && z == m ? l : INT_MAX);
             const bool stop = i == p.gamma || __shfl(tok, base + i, 64) != a;
             if (active && stop) {
                 n = i;
@@ -2111,12 +2133,12 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
         } else {
             // e and S keep row n's values once a row's walk has ended
             const double ei = active && l < V ? exp2_f64(fma((double)z, p.cd, -(double)m * p.cd), p.ex) : 0.0;
-            const double Si = row_sum16(ei);
+            const double Si = row_sum<RL>(ei);
             if (active) { e = ei; S = Si; }
             if (active && l == i) st_S = Si;
             if (i == p.gamma) break;  // the rows still walking accepted every draft
             const int x = __shfl(tok, base + i, 64);
-            const double ex = __shfl(ei, base + (x & 15), 64);  // e_x: lane x of the row holds it (x < V <= 16)
+            const double ex = __shfl(ei, base + (x & (RL - 1)), 64);  // e_x: lane x of the row holds it (x < V <= RL)
             const float ui = __shfl(ul, base + i, 64);
             double P = 0.0, Q = 0.0;
             bool rej = false;
@@ -2149,20 +2171,20 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
             w = l < V ? fmax(0.0, e * (1.0 / S) - p.len * q) : 0.0;
         }
         if (!(walked && resid)) w = walked ? e : 0.0;
-        Zr = row_sum16(walked && resid ? w : 0.0);
+        Zr = row_sum<RL>(walked && resid ? w : 0.0);
         const bool use_resid = walked && resid && Zr > kResidEps;
         if (walked && resid && !use_resid) w = e;
         const double total = use_resid ? Zr : S;
         const double target = (double)__shfl(ul, base + p.gamma, 64) * total;
-        const double incl = row_incl_scan16(w);
+        const double incl = row_incl_scan<RL>(w);
         const uint64_t hit = __ballot(walked && w > 0.0 && incl > target);
-        const uint32_t hr = (uint32_t)((hit >> (16 * r)) & 0xffffull);
+        const uint32_t hr = (uint32_t)((hit >> (RL * r)) & kRowBits);
         const uint64_t pos = __ballot(walked && w > 0.0);
-        const uint32_t pr = (uint32_t)((pos >> (16 * r)) & 0xffffull);
+        const uint32_t pr = (uint32_t)((pos >> (RL * r)) & kRowBits);
         if (walked) t = hr ? __builtin_ctz(hr) : (pr ? 31 - __builtin_clz(pr) : -1);
         if (walked && resid) Z = Zr;
         // p_n(t) = e_t / S: lane t of this row holds e_t
-        const double et = __shfl(e, base + (t & 15), 64);
+        const double et = __shfl(e, base + (t & (RL - 1)), 64);
         if (walked && t >= 0) pout = et / S;
     }
 
@@ -2189,16 +2211,20 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
 }
 
 template <int DT, int PT>
-bool launch_small_t(bool greedy, bool tiny, int grid, const Params& p, hipStream_t s)
+bool launch_small_t(bool greedy, int tiny_lanes, int grid, const Params& p, hipStream_t s)
 {
-    if (tiny) {  // four sequences per wave
-        // (the rows of a sequence held in registers: 8 when gamma + 1 <= 8, else 16)
-        if (p.gamma + 1 <= 8) {
-            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, 8>), dim3(grid), dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((k_tiny<DT, PT, false, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+    if (tiny_lanes) {
+        // k_tiny: rows of tiny_lanes lanes (8: eight sequences per wave, 16:
+        // four); the rows of a sequence held in registers: 8 when gamma + 1 <= 8, else 16
+        if (tiny_lanes == 8) {
+            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, 8, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_tiny<DT, PT, false, 8, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+        } else if (p.gamma + 1 <= 8) {
+            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, 8, 16>), dim3(grid), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_tiny<DT, PT, false, 8, 16>), dim3(grid), dim3(kThreads), 0, s, p);
         } else {
-            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, kTinyV>), dim3(grid), dim3(kThreads), 0, s, p);
-            else hipLaunchKernelGGL((k_tiny<DT, PT, false, kTinyV>), dim3(grid), dim3(kThreads), 0, s, p);
+            if (greedy) hipLaunchKernelGGL((k_tiny<DT, DT, true, kTinyV, 16>), dim3(grid), dim3(kThreads), 0, s, p);
+            else hipLaunchKernelGGL((k_tiny<DT, PT, false, kTinyV, 16>), dim3(grid), dim3(kThreads), 0, s, p);
         }
         return hipGetLastError() == hipSuccess;
     }
@@ -2207,12 +2233,12 @@ bool launch_small_t(bool greedy, bool tiny, int grid, const Params& p, hipStream
     return hipGetLastError() == hipSuccess;
 }
 
-bool launch_small(int dt, int pt, bool greedy, bool tiny, int grid, const Params& p, hipStream_t s)
+bool launch_small(int dt, int pt, bool greedy, int tiny_lanes, int grid, const Params& p, hipStream_t s)
 {
-    if (dt == SV_FP32 && (greedy || pt == SV_FP32)) return launch_small_t<SV_FP32, SV_FP32>(greedy, tiny, grid, p, s);
-    if (dt == SV_FP32) return launch_small_t<SV_FP32, SV_BF16>(greedy, tiny, grid, p, s);
-    if (greedy || pt == SV_FP32) return launch_small_t<SV_BF16, SV_FP32>(greedy, tiny, grid, p, s);
-    return launch_small_t<SV_BF16, SV_BF16>(greedy, tiny, grid, p, s);
+    if (dt == SV_FP32 && (greedy || pt == SV_FP32)) return launch_small_t<SV_FP32, SV_FP32>(greedy, tiny_lanes, grid, p, s);
+    if (dt == SV_FP32) return launch_small_t<SV_FP32, SV_BF16>(greedy, tiny_lanes, grid, p, s);
+    if (greedy || pt == SV_FP32) return launch_small_t<SV_BF16, SV_FP32>(greedy, tiny_lanes, grid, p, s);
+    return launch_small_t<SV_BF16, SV_BF16>(greedy, tiny_lanes, grid, p, s);
 }
 
 // ---------------------------------------------------------------- host dispatch
@@ -2282,6 +2308,8 @@ struct Plan {
     long long gridb;   // telemetry sweep: B * gamma * nchb
     bool small;        // V <= 512 without telemetry: one launch of k_small or k_tiny
     bool tiny;         //   k_tiny: V <= 16 and gamma < 16
+    int tiny_lanes;    //   its lanes per sequence: 8 when V <= 8 and gamma < 8, else 16
+    int seqs_per_wg;   //   sequences per workgroup of the one launch
     long long grid_small;
     bool helpers;
     int status;
@@ -2300,7 +2328,9 @@ Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, b
     q.gridb = tele ? (long long)batch * gamma * L.nchb : 0;
     q.small = vocab <= kSmallV && !tele;
     q.tiny = q.small && vocab <= kTinyV && gamma < 16;
-    q.grid_small = q.tiny ? ((long long)batch + 4 * kWaves - 1) / (4 * kWaves) : ((long long)batch + kWaves - 1) / kWaves;
+    q.tiny_lanes = vocab <= 8 && gamma + 1 <= 8 ? 8 : 16;
+    q.seqs_per_wg = q.tiny ? (64 / q.tiny_lanes) * kWaves : kWaves;
+    q.grid_small = ((long long)batch + q.seqs_per_wg - 1) / q.seqs_per_wg;
     q.status = SV_OK;
     if (q.nch1 > 0xffff || q.gridh > INT_MAX || q.grid2 > INT_MAX || q.gridb > INT_MAX) q.status = SV_ERR_TOO_LARGE;
     if (!greedy && batch > kMaxListed) q.status = SV_ERR_TOO_LARGE;
@@ -2501,7 +2531,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     bool ok;
     if (q.small) {
         // one launch, one wave per sequence (the workspace is not touched)
-        ok = launch_small(logits_dtype, probs_dtype, greedy, q.tiny, (int)q.grid_small, p, s);
+        ok = launch_small(logits_dtype, probs_dtype, greedy, q.tiny ? q.tiny_lanes : 0, (int)q.grid_small, p, s);
         if (ok && ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) ok = false;
     } else if (greedy) {
         ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)q.grid1, batch, p, s, ev_mid)

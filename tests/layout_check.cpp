@@ -91,10 +91,14 @@ static void check_shape(int B, int gamma, int V, int ldt, int pdt, bool greedy, 
     CHECK(q.gridh <= INT_MAX && q.grid2 <= INT_MAX && q.gridb <= INT_MAX, "grids fit an int");
 
     if (q.small) {
-        // k_small: one wave per sequence; k_tiny: four per wave
-        const long long per = q.tiny ? 4LL * kWaves : (long long)kWaves;
+        // k_small: one wave per sequence; k_tiny: four (rows of 16 lanes) or
+        // eight (rows of 8) per wave, every entry of a row in a lane of its own
+        const long long per = q.tiny ? (64LL / q.tiny_lanes) * kWaves : (long long)kWaves;
+        CHECK(q.seqs_per_wg == per, "sequences per workgroup");
         CHECK(q.grid_small * per >= B && (q.grid_small - 1) * per < B, "B=%d: small grid %lld", B, q.grid_small);
-        CHECK(V <= (q.tiny ? kTinyV : kSmallV), "V=%d on the one-launch path", V);
+        CHECK(V <= (q.tiny ? q.tiny_lanes : kSmallV), "V=%d on the one-launch path", V);
+        CHECK(!q.tiny || q.tiny_lanes == 16 || gamma + 1 <= 8, "an 8-lane row holds the gamma + 1 uniforms");
+        CHECK(!q.tiny || gamma + 1 <= 16, "the tiny path holds at most 16 rows per sequence");
         return;
     }
 

@@ -144,3 +144,19 @@ def test_four_sequences_per_wave(V, gamma):
     _check(d, "greedy")
     db = synth.make_inputs("c5", 1900 + V + gamma, B=21, gamma=gamma, V=V)
     _check(db)
+
+
+@pytest.mark.parametrize("V,gamma", [(8, 7), (1, 1), (5, 3), (8, 4), (2, 7)])
+def test_eight_sequences_per_wave(V, gamma):
+    """V <= 8 and gamma + 1 <= 8 run eight sequences per wave (one per 8-lane
+    half row): a ragged batch, invalid drafts, lenience, greedy, bf16."""
+    d = synth.make_inputs("c2", 2000 + V * 16 + gamma, B=45, gamma=gamma, V=V)
+    d["draft_tokens"][9, gamma - 1] = V
+    d["draft_tokens"][30, 0] = -1
+    for lenience in (1.0, 0.3):
+        g, _ = _check(d, lenience=lenience)
+        for b in (9, 30):
+            assert g["n_accepted"][b] == -1 and np.all(g["out_tokens"][b] == -1)
+    _check(d, "greedy")
+    db = synth.make_inputs("c5", 2100 + V + gamma, B=29, gamma=gamma, V=V)
+    _check(db)
