@@ -821,11 +821,12 @@ __device__ __forceinline__ void draw_wave_sums(const Params& p, const Raw8 (&zr)
     }
 }
 
-// COUNTED (second launch): the sums go out with device-scope exchanges and
-// the wave counts itself in; returns true in the wave whose count reaches
-// `target` (the sequence's wave tasks in that launch), which completes the
-// sequence's draw sums.  Otherwise (first launch) plain stores, which the
-// second launch reads after the kernel boundary.
+// COUNTED (the last launch): the sums go out with device-scope exchanges
+// and the wave counts itself in; returns true in the wave whose count
+// reaches `target` (the sequence's wave tasks in that launch), which
+// completes the sequence's draw sums.  Otherwise (the first launch's draw
+// helpers, the telemetry sweep) plain stores with a done mark, which the
+// last launch reads after the kernel boundary.
 template <int DT, int PT, bool VEC2, bool COUNTED>
 __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_t target)
 {
@@ -1587,8 +1588,9 @@ __global__ __launch_bounds__(kThreads) void k_beta_merge(const Params p)
 
 // ------------------------------------------------------------ sample, launch 2
 
-// nch2 workgroups per sequence.  The first launch's helpers took draw
-// chunks 0 .. L1-1 of a sequence (its claim count, final now); chunk L1 + j
+// The last launch of telemetry calls, nch2 workgroups per sequence.  The
+// telemetry sweep took draw chunks 0 .. L1-1 of a sequence (its claim count,
+// final now: the sweep's workgroups of the rejected row n sum them); chunk L1 + j
 // goes to the sequence's workgroup j, and a workgroup with no chunk left
 // returns after reading that count.  Workgroup i < B is workgroup 0 of the
 // sequence whose n became known (B-1-i)-th; the others (nch2 - 1 per
