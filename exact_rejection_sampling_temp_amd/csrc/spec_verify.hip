@@ -1643,8 +1643,8 @@ __global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
     __shared__ int sm_ok, sm_left;
     const int b = (int)blockIdx.x;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint64_t all = rows_mask(p.gamma);
-    if ((p.ctl[b].dec & all) != all) return;  // (every sequence is decided in the first launch)
+    // (every sequence is decided, and listed, in the first launch: the
+    // decider of each position up to the first rejection takes part)
     const uint32_t rank = (uint32_t)(p.ctl[b].retire >> 32);  // its place in the ready list
     if (w == 0) {
         const bool ok = finish_wave<DT, PT, VEC2, true>(p, b);
