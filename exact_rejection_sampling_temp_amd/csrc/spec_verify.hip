@@ -397,7 +397,10 @@ __device__ void block_amax(float& v, int& i, float* smf, int* smi)
 }
 
 // 2^a in double for a <= 0, relative error below 5.6e-11 (the draw's token
-// boundaries are judged in a 1e-9 window): a = k + f with k the nearest
+// boundaries are judged in a 1e-9 relative window; a residual boundary,
+// which subtracts l q_v from each p_v, carries the error as an absolute one,
+// so its relative error grows as the target's mass on the residual's support
+// over the residual mass): a = k + f with k the nearest
 // integer (rounded by adding 1.5 * 2^52, which leaves k in the low word) and
 // |f| <= 1/2; 2^f by the degree-7 polynomial interpolating it at the 8
 // Chebyshev nodes of [-1/2, 1/2] (seven fused multiply-adds, the constant

@@ -140,7 +140,12 @@ def check_aux(gpu: dict, ref: dict, rtol_p: float):
     np.testing.assert_array_equal(gpu["row_max"][rows].astype(np.float64), ref["row_max"][rows])
     np.testing.assert_allclose(gpu["row_sum"][rows], ref["row_sum"][rows], rtol=rtol_p)
     same = valid & (gpu["n_accepted"] == ref["n_accepted"]) & (ref["n_accepted"] < G)
-    np.testing.assert_allclose(gpu["resid_mass"][same], ref["resid_mass"][same], rtol=1e-9, atol=1e-15)
+    # Z = sum over the support A of (p_v - l q_v): each p_v carries the
+    # kernel's exp2 error (<= 5.6e-11 relative, twice that after dividing by
+    # S), and the subtraction keeps it absolute, so Z is off by up to
+    # ~1.1e-10 * P(A) <= 1.1e-10 whatever Z is; relative to Z that grows as
+    # P(A) / Z where the draft nearly matches the target on A
+    np.testing.assert_allclose(gpu["resid_mass"][same], ref["resid_mass"][same], rtol=1e-9, atol=2e-10)
     # p_n of the drawn token, where both sides drew the same token at the same n
     if "p_out" in gpu:
         nn = np.clip(ref["n_accepted"], 0, G)
