@@ -2248,14 +2248,15 @@ bool launch_small(int dt, int pt, bool greedy, int tiny_lanes, int grid, const P
 
 // ---------------------------------------------------------------- host dispatch
 
+// lds1: dynamic LDS of the first launch, which only caps its workgroups per CU
 template <int DT, int PT>
-void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream_t s, hipEvent_t ev_mid,
-                     hipEvent_t ev_tele, bool* ok)
+void launch_sample_t(int vmode, int grid1, unsigned lds1, int grid2, const Params& p, hipStream_t s,
+                     hipEvent_t ev_mid, hipEvent_t ev_tele, bool* ok)
 {
     switch (vmode) {
-    case 2: hipLaunchKernelGGL((k_main_sample<DT, PT, 2>), dim3(grid1), dim3(kThreads), 0, s, p); break;
-    case 1: hipLaunchKernelGGL((k_main_sample<DT, PT, 1>), dim3(grid1), dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_main_sample<DT, PT, 0>), dim3(grid1), dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((k_main_sample<DT, PT, 2>), dim3(grid1), dim3(kThreads), lds1, s, p); break;
+    case 1: hipLaunchKernelGGL((k_main_sample<DT, PT, 1>), dim3(grid1), dim3(kThreads), lds1, s, p); break;
+    default: hipLaunchKernelGGL((k_main_sample<DT, PT, 0>), dim3(grid1), dim3(kThreads), lds1, s, p); break;
     }
     if (hipGetLastError() != hipSuccess) { *ok = false; return; }
     if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) { *ok = false; return; }
@@ -2277,14 +2278,14 @@ void launch_sample_t(int vmode, int grid1, int grid2, const Params& p, hipStream
     if (hipGetLastError() != hipSuccess) *ok = false;
 }
 
-bool launch_sample(int dt, int pt, int vmode, int grid1, int grid2, const Params& p, hipStream_t s,
+bool launch_sample(int dt, int pt, int vmode, int grid1, unsigned lds1, int grid2, const Params& p, hipStream_t s,
                    hipEvent_t ev_mid, hipEvent_t ev_tele)
 {
     bool ok = true;
-    if (dt == SV_FP32 && pt == SV_FP32) launch_sample_t<SV_FP32, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
-    if (dt == SV_FP32 && pt == SV_BF16) launch_sample_t<SV_FP32, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
-    if (dt == SV_BF16 && pt == SV_FP32) launch_sample_t<SV_BF16, SV_FP32>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
-    if (dt == SV_BF16 && pt == SV_BF16) launch_sample_t<SV_BF16, SV_BF16>(vmode, grid1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_FP32 && pt == SV_FP32) launch_sample_t<SV_FP32, SV_FP32>(vmode, grid1, lds1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_FP32 && pt == SV_BF16) launch_sample_t<SV_FP32, SV_BF16>(vmode, grid1, lds1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_BF16 && pt == SV_FP32) launch_sample_t<SV_BF16, SV_FP32>(vmode, grid1, lds1, grid2, p, s, ev_mid, ev_tele, &ok);
+    if (dt == SV_BF16 && pt == SV_BF16) launch_sample_t<SV_BF16, SV_BF16>(vmode, grid1, lds1, grid2, p, s, ev_mid, ev_tele, &ok);
     return ok;
 }
 
@@ -2342,6 +2343,35 @@ Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, b
     return q;
 }
 
+// Row blocks resident per CU in the first launch of a sample call.  Rows past
+// a sequence's first rejection are skipped only once that rejection is known,
+// and position k's blocks are dispatched after those of every earlier
+// position; with the batch resident several positions deep, the later
+// positions stream rows that the earlier ones are about to make unneeded.
+// About 1.5 positions of row blocks at a time (B * nch1 blocks a position)
+// keeps the chip fed while the decisions stay ahead: ceil(1.5 * blocks / CUs),
+// between 3 and 8 (8: no cap, the kernel's own limit at <= 64 VGPRs).
+constexpr int kMinRowWgsPerCu = 3, kMaxRowWgsPerCu = 8;
+constexpr int kStaticLdsMargin = 256;  // above the first launch's static LDS (< 100 bytes)
+
+inline int row_wgs_per_cu(long long blocks_per_position, int n_cu)
+{
+    if (n_cu <= 0) return kMaxRowWgsPerCu;
+    const long long n = (3 * blocks_per_position + 2LL * n_cu - 1) / (2LL * n_cu);
+    return (int)(n < kMinRowWgsPerCu ? kMinRowWgsPerCu : n > kMaxRowWgsPerCu ? kMaxRowWgsPerCu : n);
+}
+
+// Dynamic LDS that holds a workgroup to `wgs` per CU (0: no cap): each takes
+// lds_cu / (wgs + 1/2) bytes, static LDS included, so `wgs` of them fit and
+// one more does not; the slack, lds_cu / (2 wgs + 1), covers the allocation
+// granule.
+inline unsigned cap_lds_bytes(int wgs, int lds_cu, int lds_block_max)
+{
+    if (wgs >= kMaxRowWgsPerCu || wgs < 1 || lds_cu <= 0) return 0u;
+    const long long dyn = 2LL * lds_cu / (2 * wgs + 1) - kStaticLdsMargin;
+    return dyn > 0 && dyn <= lds_block_max ? (unsigned)dyn : 0u;
+}
+
 // The checks of every verify entry point that need no workspace and no HIP
 // call; SV_OK or the status to return.
 int check_args(int batch, int gamma, int vocab, const void* target_logits, int logits_dtype,
@@ -2384,6 +2414,31 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's CU count and LDS sizes, asked once per device; zeros
+// when they cannot be had (the first launch then runs uncapped).
+struct DevProps {
+    int n_cu, lds_cu, lds_block;
+};
+std::mutex g_props_mu;
+DevProps g_props[kMaxDevices] = {};
+
+DevProps dev_props()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DevProps{0, 0, 0};
+    std::lock_guard<std::mutex> lock(g_props_mu);
+    DevProps& d = g_props[dev];
+    if (d.n_cu == 0) {
+        DevProps q{0, 0, 0};
+        if (hipDeviceGetAttribute(&q.n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&q.lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&q.lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return DevProps{0, 0, 0};
+        d = q;
+    }
+    return d;
+}
 
 // The current device's scratch address, fetched and zero-filled (with a
 // kernel, on `s`) on the first call on that device; nullptr on failure.
@@ -2542,7 +2597,14 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
         ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)q.grid1, batch, p, s, ev_mid)
                                      : launch_greedy_t<SV_FP32>(vec, (int)q.grid1, batch, p, s, ev_mid);
     } else {
-        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)q.gridh, (int)q.grid2, p, s, ev_mid,
+        // (the cap only where rows can be skipped: not with the telemetry,
+        // which streams every row)
+        unsigned lds1 = 0;
+        if (q.helpers) {
+            const DevProps dp = dev_props();
+            lds1 = cap_lds_bytes(row_wgs_per_cu((long long)batch * nch1, dp.n_cu), dp.lds_cu, dp.lds_block);
+        }
+        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)q.gridh, lds1, (int)q.grid2, p, s, ev_mid,
                            extras ? (hipEvent_t)extras->ev_tele : nullptr);
     }
     if (!ok) return SV_ERR_LAUNCH;

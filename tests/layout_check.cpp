@@ -169,8 +169,39 @@ static void check_shape(int B, int gamma, int V, int ldt, int pdt, bool greedy, 
     }
 }
 
+// The first launch's occupancy cap: 3..8 row blocks per CU, growing with the
+// blocks of one position; the dynamic LDS lets exactly that many workgroups
+// share a CU (static LDS up to 100 bytes, allocation granules up to 1280).
+static void check_occupancy_cap()
+{
+    for (int n_cu : {1, 80, 256, 304}) {
+        int prev = 0;
+        for (long long bpp = 1; bpp < (1LL << 26); bpp = bpp * 3 / 2 + 1) {
+            const int w = row_wgs_per_cu(bpp, n_cu);
+            CHECK(w >= kMinRowWgsPerCu && w <= kMaxRowWgsPerCu && w >= prev, "n_cu=%d bpp=%lld -> %d", n_cu, bpp, w);
+            // between the bounds, w = ceil(1.5 * bpp / n_cu)
+            if (w > kMinRowWgsPerCu && w < kMaxRowWgsPerCu)
+                CHECK(2LL * (w - 1) * n_cu < 3 * bpp && 3 * bpp <= 2LL * w * n_cu, "n_cu=%d bpp=%lld", n_cu, bpp);
+            prev = w;
+        }
+    }
+    // 256 CUs: c4 (256 sequences x 10 chunks) uncapped, c3 and c5 (512 blocks a position) at 3
+    CHECK(row_wgs_per_cu(2560, 256) == 8 && row_wgs_per_cu(512, 256) == 3 && row_wgs_per_cu(640, 256) == 4,
+          "the measured shapes");
+    for (int lds : {65536, 163840}) {
+        CHECK(cap_lds_bytes(kMaxRowWgsPerCu, lds, lds) == 0u, "no cap at 8");
+        for (int w = kMinRowWgsPerCu; w < kMaxRowWgsPerCu; ++w) {
+            const long long d = cap_lds_bytes(w, lds, lds);
+            const long long held = (d + 100 + 1279) / 1280 * 1280;
+            CHECK(d > 0 && w * held <= lds && (w + 1) * d > lds, "lds=%d w=%d dyn=%lld", lds, w, d);
+        }
+        CHECK(cap_lds_bytes(3, lds, 1024) == 0u, "above the per-workgroup limit: no cap");
+    }
+}
+
 int main()
 {
+    check_occupancy_cap();
     const int batches[] = {1, 2, 3, 7, 64, 255, 256, 1231, 4096, 100000, kMaxListed, kMaxListed + 1};
     const int gammas[] = {1, 2, 4, 8, 15, 16, 62, 63};
     const int vocabs[] = {1, 7, 8, 16, 17, 512, 513, 8191, 8192, 8193, 16383, 16384, 16385, 32000, 128256,
