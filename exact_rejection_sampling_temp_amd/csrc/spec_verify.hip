@@ -2290,10 +2290,10 @@ bool launch_sample(int dt, int pt, int vmode, int grid1, unsigned lds1, int grid
 }
 
 template <int DT>
-bool launch_greedy_t(bool vec, int grid1, int B, const Params& p, hipStream_t s, hipEvent_t ev_mid)
+bool launch_greedy_t(bool vec, int grid1, unsigned lds1, int B, const Params& p, hipStream_t s, hipEvent_t ev_mid)
 {
-    if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true>), dim3(grid1), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_rows_greedy<DT, false>), dim3(grid1), dim3(kThreads), 0, s, p);
+    if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true>), dim3(grid1), dim3(kThreads), lds1, s, p);
+    else hipLaunchKernelGGL((k_rows_greedy<DT, false>), dim3(grid1), dim3(kThreads), lds1, s, p);
     if (hipGetLastError() != hipSuccess) return false;
     if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) return false;
     hipLaunchKernelGGL(k_draw_greedy, dim3(B), dim3(kThreads), 0, s, p);
@@ -2343,21 +2343,24 @@ Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, b
     return q;
 }
 
-// Row blocks resident per CU in the first launch of a sample call.  Rows past
-// a sequence's first rejection are skipped only once that rejection is known,
-// and position k's blocks are dispatched after those of every earlier
-// position; with the batch resident several positions deep, the later
-// positions stream rows that the earlier ones are about to make unneeded.
-// About 1.5 positions of row blocks at a time (B * nch1 blocks a position)
-// keeps the chip fed while the decisions stay ahead: ceil(1.5 * blocks / CUs),
-// between 3 and 8 (8: no cap, the kernel's own limit at <= 64 VGPRs).
+// Row blocks resident per CU in the first launch.  Rows past a sequence's
+// first rejection are skipped only once that rejection is known, and position
+// k's blocks are dispatched after those of every earlier position; with the
+// batch resident several positions deep, the later positions stream rows that
+// the earlier ones are about to make unneeded.  A few positions of row blocks
+// at a time (B * nch1 blocks a position) keep the chip fed while the
+// decisions stay ahead: ceil(depth * blocks / CUs), between 3 and 8 (8: no
+// cap, the kernel's own limit at <= 64 VGPRs).  The depth, in half positions:
+// 3 in sample mode, 4 in greedy mode, whose rejections land sooner (any chunk
+// with an entry above the draft token's decides its position).
 constexpr int kMinRowWgsPerCu = 3, kMaxRowWgsPerCu = 8;
+constexpr int kSampleHalfPositions = 3, kGreedyHalfPositions = 4;
 constexpr int kStaticLdsMargin = 256;  // above the first launch's static LDS (< 100 bytes)
 
-inline int row_wgs_per_cu(long long blocks_per_position, int n_cu)
+inline int row_wgs_per_cu(long long blocks_per_position, int n_cu, int half_positions)
 {
     if (n_cu <= 0) return kMaxRowWgsPerCu;
-    const long long n = (3 * blocks_per_position + 2LL * n_cu - 1) / (2LL * n_cu);
+    const long long n = (half_positions * blocks_per_position + 2LL * n_cu - 1) / (2LL * n_cu);
     return (int)(n < kMinRowWgsPerCu ? kMinRowWgsPerCu : n > kMaxRowWgsPerCu ? kMaxRowWgsPerCu : n);
 }
 
@@ -2593,19 +2596,21 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
         // one launch, one wave per sequence (the workspace is not touched)
         ok = launch_small(logits_dtype, probs_dtype, greedy, q.tiny ? q.tiny_lanes : 0, (int)q.grid_small, p, s);
         if (ok && ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) ok = false;
-    } else if (greedy) {
-        ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)q.grid1, batch, p, s, ev_mid)
-                                     : launch_greedy_t<SV_FP32>(vec, (int)q.grid1, batch, p, s, ev_mid);
     } else {
-        // (the cap only where rows can be skipped: not with the telemetry,
-        // which streams every row)
+        // the first launch's cap on resident row blocks, only where rows can
+        // be skipped (the telemetry streams every row)
         unsigned lds1 = 0;
-        if (q.helpers) {
+        if (greedy || q.helpers) {
             const DevProps dp = dev_props();
-            lds1 = cap_lds_bytes(row_wgs_per_cu((long long)batch * nch1, dp.n_cu), dp.lds_cu, dp.lds_block);
+            const int depth = greedy ? kGreedyHalfPositions : kSampleHalfPositions;
+            lds1 = cap_lds_bytes(row_wgs_per_cu((long long)batch * nch1, dp.n_cu, depth), dp.lds_cu, dp.lds_block);
         }
-        ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)q.gridh, lds1, (int)q.grid2, p, s, ev_mid,
-                           extras ? (hipEvent_t)extras->ev_tele : nullptr);
+        if (greedy)
+            ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)q.grid1, lds1, batch, p, s, ev_mid)
+                                         : launch_greedy_t<SV_FP32>(vec, (int)q.grid1, lds1, batch, p, s, ev_mid);
+        else
+            ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)q.gridh, lds1, (int)q.grid2, p, s, ev_mid,
+                               extras ? (hipEvent_t)extras->ev_tele : nullptr);
     }
     if (!ok) return SV_ERR_LAUNCH;
     if (extras && extras->ev_end && hipEventRecord((hipEvent_t)extras->ev_end, s) != hipSuccess)

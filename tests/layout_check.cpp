@@ -174,19 +174,24 @@ static void check_shape(int B, int gamma, int V, int ldt, int pdt, bool greedy, 
 // share a CU (static LDS up to 100 bytes, allocation granules up to 1280).
 static void check_occupancy_cap()
 {
-    for (int n_cu : {1, 80, 256, 304}) {
-        int prev = 0;
-        for (long long bpp = 1; bpp < (1LL << 26); bpp = bpp * 3 / 2 + 1) {
-            const int w = row_wgs_per_cu(bpp, n_cu);
-            CHECK(w >= kMinRowWgsPerCu && w <= kMaxRowWgsPerCu && w >= prev, "n_cu=%d bpp=%lld -> %d", n_cu, bpp, w);
-            // between the bounds, w = ceil(1.5 * bpp / n_cu)
-            if (w > kMinRowWgsPerCu && w < kMaxRowWgsPerCu)
-                CHECK(2LL * (w - 1) * n_cu < 3 * bpp && 3 * bpp <= 2LL * w * n_cu, "n_cu=%d bpp=%lld", n_cu, bpp);
-            prev = w;
+    for (int h : {kSampleHalfPositions, kGreedyHalfPositions})
+        for (int n_cu : {1, 80, 256, 304}) {
+            int prev = 0;
+            for (long long bpp = 1; bpp < (1LL << 26); bpp = bpp * 3 / 2 + 1) {
+                const int w = row_wgs_per_cu(bpp, n_cu, h);
+                CHECK(w >= kMinRowWgsPerCu && w <= kMaxRowWgsPerCu && w >= prev, "h=%d n_cu=%d bpp=%lld -> %d", h,
+                      n_cu, bpp, w);
+                // between the bounds, w = ceil(h/2 * bpp / n_cu)
+                if (w > kMinRowWgsPerCu && w < kMaxRowWgsPerCu)
+                    CHECK(2LL * (w - 1) * n_cu < h * bpp && h * bpp <= 2LL * w * n_cu, "h=%d n_cu=%d bpp=%lld", h,
+                          n_cu, bpp);
+                prev = w;
+            }
         }
-    }
-    // 256 CUs: c4 (256 sequences x 10 chunks) uncapped, c3 and c5 (512 blocks a position) at 3
-    CHECK(row_wgs_per_cu(2560, 256) == 8 && row_wgs_per_cu(512, 256) == 3 && row_wgs_per_cu(640, 256) == 4,
+    // 256 CUs: c4 (256 sequences x 10 chunks) uncapped; c3 and c5 (512 blocks
+    // a position) at 3 in sample mode and 4 in greedy mode
+    CHECK(row_wgs_per_cu(2560, 256, kSampleHalfPositions) == 8 && row_wgs_per_cu(2560, 256, kGreedyHalfPositions) == 8 &&
+              row_wgs_per_cu(512, 256, kSampleHalfPositions) == 3 && row_wgs_per_cu(512, 256, kGreedyHalfPositions) == 4,
           "the measured shapes");
     for (int lds : {65536, 163840}) {
         CHECK(cap_lds_bytes(kMaxRowWgsPerCu, lds, lds) == 0u, "no cap at 8");
