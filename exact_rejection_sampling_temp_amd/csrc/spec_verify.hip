@@ -107,6 +107,7 @@ constexpr int kChunkB = 8192;                       // telemetry sweep: row elem
 constexpr int kGroupsB = kChunkB / (8 * kThreads);  // groups of 8 per thread
 static_assert(kChunkB == kChunk2, "a telemetry workgroup covers exactly one draw chunk");
 static_assert(kChunk2 == kSubW * kWaves, "a draw chunk is one sub-chunk per wave");
+static_assert(kSubPerWave == kWaves, "the last launch scans a sub-chunk's groups one per wave");
 // Bound of a draw helper's wait for its sequence to be resolved (polls ~1 us
 // apart under load; the row stage of a call takes ~100 us at most).
 constexpr int kHelpPolls = 1 << 14;
@@ -964,7 +965,11 @@ __device__ __forceinline__ void retire_wave(const Params& p, int b, uint32_t use
 // group at a time with every weight recomputed exactly, finds the token.
 // MARKS: the sums come from the first launch's draw helpers, each with its
 // done mark; if a mark is missing the wave writes nothing and returns false.
-template <int DT, int PT, bool VEC2, bool MARKS>
+// PAR: every wave of the workgroup runs this on the same data (so all take
+// the same branches and meet at the barriers), wave w scans group w of the
+// sub-chunk and the groups' totals are combined through LDS in index order,
+// the sequential scan's arithmetic unchanged; wave 0 writes the outputs.
+template <int DT, int PT, bool VEC2, bool MARKS, bool PAR = false>
 __device__ bool finish_wave(const Params& p, int b)
 {
     const int lane = threadIdx.x & 63;
@@ -1086,21 +1091,79 @@ __device__ bool finish_wave(const Params& p, int b)
                            (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
         const double nMcd = -(double)__shfl(st.m, n, 64) * p.cd;  // lane n holds row n's statistics
         double rem = target - pre;
+        int s_from = js * kSubPerWave;  // the first group the loop below scans
+        if constexpr (PAR) {
+            __shared__ double sm_tot[kWaves];
+            __shared__ int sm_first, sm_t;
+            const int w = (int)(threadIdx.x >> 6);
+            if (js >= 0) {  // (uniform across the workgroup)
+                const int s = js * kSubPerWave + w;
+                const int idx = s * kSub + lane * 8;
+                const bool have = s < p.nsub * kSubPerWave && s * kSub < p.V;
+                Raw8 zr{}, qr{};
+                if (have) {
+                    zr = load_group<DT, VEC2>(zrow, idx, p.V);
+                    if (use_resid) qr = load_group<PT, VEC2>(qrow, idx, p.V);
+                }
+                double wv[8], lt = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    wv[e] = have && idx + e < p.V ? draw_weight(p, use_resid, raw8_elem<DT>(zr, e),
+                                                                use_resid ? raw8_elem<PT>(qr, e) : 0.0f, nMcd, invS)
+                                                  : 0.0;
+                    lt += wv[e];
+                }
+                const double incl = wave_incl_scan_dpp(lt);
+                if (lane == 63) sm_tot[w] = incl;
+                if (threadIdx.x == 0) sm_first = kWaves;
+                __syncthreads();
+                double rw = rem;  // the target less the groups before this one, subtracted in order
+                for (int h = 0; h < w; ++h) rw -= sm_tot[h];
+                const int L = first_lane(__ballot(have && lt > 0.0 && incl > rw));
+                if (L >= 0 && lane == 0) atomicMin(&sm_first, w);
+                __syncthreads();
+                const int wf = sm_first;
+                if (wf < kWaves) {
+                    if (w == wf) {
+                        double excl = __shfl_up(incl, 1, 64);
+                        if (lane == 0) excl = 0.0;
+                        int found = -1, ipos = -1;
+                        double c = excl;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            if (found < 0 && wv[e] > 0.0) {
+                                if (c + wv[e] > rw) found = e;
+                                else { ipos = e; c += wv[e]; }
+                            }
+                        }
+                        if (found < 0) found = ipos;
+                        const int tt = s * kSub + L * 8 + __shfl(found, L, 64);
+                        if (lane == 0) sm_t = tt;
+                    }
+                    __syncthreads();
+                    t = sm_t;
+                } else {
+                    // past the sub-chunk only by rounding: on from the next group
+                    for (int h = 0; h < kWaves; ++h) rem -= sm_tot[h];
+                    s_from = (js + 1) * kSubPerWave;
+                }
+            }
+        }
         // the sub-chunk's groups, all loads in flight at once
         Raw8 zs[kSubPerWave], qs[kSubPerWave];
-        if (js >= 0) {
+        if (!PAR && js >= 0) {
 #pragma unroll
             for (int g = 0; g < kSubPerWave; ++g) {
                 zs[g] = load_group<DT, VEC2>(zrow, (js * kSubPerWave + g) * kSub + lane * 8, p.V);
                 if (use_resid) qs[g] = load_group<PT, VEC2>(qrow, (js * kSubPerWave + g) * kSub + lane * 8, p.V);
             }
         }
-        for (int s = js * kSubPerWave; js >= 0 && s < p.nsub * kSubPerWave && t < 0; ++s) {
+        for (int s = s_from; js >= 0 && s < p.nsub * kSubPerWave && t < 0; ++s) {
             const int idx = s * kSub + lane * 8;
             if (s * kSub >= p.V) break;
             const int g = s - js * kSubPerWave;
             Raw8 zr{}, qr{};
-            if (g < kSubPerWave) {
+            if (!PAR && g < kSubPerWave) {
                 // (a constant index into the prefetched groups)
 #pragma unroll
                 for (int h = 0; h < kSubPerWave; ++h)
@@ -1178,6 +1241,7 @@ __device__ bool finish_wave(const Params& p, int b)
     }
 
     // outputs and telemetry
+    if (PAR && threadIdx.x >= 64) return true;
     if (lane < G1) {
         int32_t o;
         if (invalid) o = -1;
@@ -1634,7 +1698,7 @@ __global__ __launch_bounds__(kThreads) void k_rest_sample(const Params p)
 }
 
 // The last launch when the first launch carries draw helpers: workgroup b
-// finishes sequence b.  Wave 0 runs the draw from the helpers' sums; should a
+// finishes sequence b.  Its waves run the draw from the helpers' sums; should a
 // sub-chunk lack its done mark (its helper's wait ran out), the workgroup
 // computes every unmarked sub-chunk, counting them out, and the wave that
 // completes the count runs the draw.  Then the sequence is cleared.  The
@@ -1649,9 +1713,11 @@ __global__ __launch_bounds__(kThreads) void k_finish_sample(const Params p)
     // (every sequence is decided, and listed, in the first launch: the
     // decider of each position up to the first rejection takes part)
     const uint32_t rank = (uint32_t)(p.ctl[b].retire >> 32);  // its place in the ready list
-    if (w == 0) {
-        const bool ok = finish_wave<DT, PT, VEC2, true>(p, b);
-        if (lane == 0) sm_ok = ok ? 1 : 0;
+    {
+        // every wave (the four groups of the chosen sub-chunk are scanned side
+        // by side); each returns the same result
+        const bool ok = finish_wave<DT, PT, VEC2, true, true>(p, b);
+        if (threadIdx.x == 0) sm_ok = ok ? 1 : 0;
     }
     if (threadIdx.x == 0) sm_left = 0;
     __syncthreads();
