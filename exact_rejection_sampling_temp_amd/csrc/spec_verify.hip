@@ -98,6 +98,14 @@ constexpr int kChunkFp32 = kEptFp32 * kThreads;  // 8192 elements
 constexpr int kSub = 512;                           // elements of a group
 constexpr int kSubPerWave = 4;                      // groups of a wave task (one sub-chunk)
 constexpr int kSubPerPass = 2;  // first launch (the helpers share SIMDs with the row stage)
+// Up to this many sub-chunks in a batch, the first launch's draw helpers take
+// one sub-chunk each (a group per wave) rather than a draw chunk each: four
+// times the helpers, each a quarter as long, for batches whose helpers all fit
+// on the chip at once (~one round of resident workgroups at the cap of 3 per
+// CU), where the draws sit on the call's critical path.  Above it the extra
+// helpers' fixed costs (the ready-list poll, the row statistics) outweigh the
+// shorter draws.
+constexpr long long kFineHelpers = 1024;
 constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16 groups in a draw chunk
 constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
 constexpr int kSubW = kSub * kSubPerWave;           // 2048 elements of a sub-chunk
@@ -667,6 +675,7 @@ struct Params {
     Exp2Coef ex;       // kExp2Coef
     int rows_grid;     // first launch: row blocks (G1 * B * nch1); the draw helpers follow
     int help_polls;    // bound of a draw helper's wait for its sequence
+    int fine;          // 1: one draw helper per sub-chunk (a wave per group), else one per draw chunk
     int polls_slot;    // bound of a merge's wait for a partial slot
     int drop_slot;     // test hook: >= 0 makes chunk 0 of that position withhold its
                        // partial, so that the merge's bounded wait runs out
@@ -697,6 +706,13 @@ __host__ __device__ __forceinline__ DrawTask helper_task(int j, int nch2)
 }
 // the sub-chunk (kSubW elements, one wave task) of wave w of draw chunk c2
 __host__ __device__ __forceinline__ int wave_sub(int c2, int w) { return c2 * kWaves + w; }
+// fine helpers: helper j takes sub-chunk j % nsub of the (j / nsub)-th listed
+// sequence, its wave w group w of that sub-chunk
+__host__ __device__ __forceinline__ DrawTask fine_task(int j, int nsub)
+{
+    const int r = j / nsub;
+    return DrawTask{r, j - r * nsub};
+}
 struct BetaBlock {
     int b, i, c;  // sequence, position, telemetry chunk
 };
@@ -888,6 +904,38 @@ __device__ bool draw_wave(const Params& p, int b, int s0, uint64_t mask, uint64_
         return __builtin_amdgcn_readfirstlane(last) != 0u;
     }
     return false;
+}
+
+// Group grp (kSub elements) of the draw row of sequence b, n from `mask`:
+// the wave's totals of E, EA, QA (see draw_wave_load), for a fine helper.
+template <int DT, int PT, bool VEC2>
+__device__ void draw_group(const Params& p, int b, int grp, uint64_t mask, double& E, double& EA, double& QA)
+{
+    const int n = first_reject(mask, p.gamma);
+    const bool resid = n < p.gamma;
+    const int64_t row = (int64_t)b * (p.gamma + 1) + n;
+    const void* zrow = static_cast<const char*>(p.logits) + (size_t)row * p.V * (DT == SV_BF16 ? 2 : 4);
+    const void* qrow = static_cast<const char*>(p.probs) +
+                       (size_t)((int64_t)b * p.gamma + (resid ? n : 0)) * p.V * (PT == SV_BF16 ? 2 : 4);
+    E = EA = QA = 0.0;
+    if (!(mask & kInvalidBit) && grp * kSub < p.V) {
+        Raw8 zr[1], qr[1];
+        draw_wave_load<DT, PT, VEC2, 1>(p, zrow, qrow, resid, grp, zr, qr);
+        const uint64_t* sw = reinterpret_cast<const uint64_t*>(p.stats + row);
+        const double nMcd = -(double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
+        const double S_row = p.len * __longlong_as_double((long long)ld_agent(sw + 1));
+        const bool full = (grp + 1) * kSub <= p.V;
+        if (resid) {
+            if (full) draw_wave_sums<DT, PT, VEC2, true, true, 1>(p, zr, qr, grp, nMcd, S_row, E, EA, QA);
+            else draw_wave_sums<DT, PT, VEC2, true, false, 1>(p, zr, qr, grp, nMcd, S_row, E, EA, QA);
+        } else {
+            if (full) draw_wave_sums<DT, PT, VEC2, false, true, 1>(p, zr, qr, grp, nMcd, S_row, E, EA, QA);
+            else draw_wave_sums<DT, PT, VEC2, false, false, 1>(p, zr, qr, grp, nMcd, S_row, E, EA, QA);
+        }
+    }
+    E = wave_sum(E);
+    EA = wave_sum(EA);
+    QA = wave_sum(QA);
 }
 
 // Element i of a row of logits or probabilities, as float.
@@ -1290,7 +1338,8 @@ template <int DT, int PT, bool VEC2>
 __device__ void help_draw(const Params& p, int j)
 {
     __shared__ uint32_t sm_he;
-    const DrawTask task = helper_task(j, p.nch2);
+    __shared__ double sm_g[kWaves][3];
+    const DrawTask task = p.fine ? fine_task(j, p.nsub) : helper_task(j, p.nch2);
     const int r = task.r;
     if (threadIdx.x == 0) {
         uint32_t e = 0;
@@ -1307,6 +1356,28 @@ __device__ void help_draw(const Params& p, int j)
     if (e == 0u || b >= p.B || n > p.gamma) return;
     // (a mask with n's reject bit alone: the draw's row and residual follow from n)
     const uint64_t mask = n < p.gamma ? 1ull << n : 0ull;
+    if (p.fine) {
+        // sub-chunk task.c2, a group per wave, the group totals added in group order
+        const int w = (int)(threadIdx.x >> 6);
+        double E, EA, QA;
+        draw_group<DT, PT, VEC2>(p, b, task.c2 * kSubPerWave + w, mask, E, EA, QA);
+        if ((threadIdx.x & 63) == 0) {
+            sm_g[w][0] = E;
+            sm_g[w][1] = EA;
+            sm_g[w][2] = QA;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double e = 0.0, ea = 0.0, qa = 0.0;
+            for (int i = 0; i < kWaves; ++i) {
+                e += sm_g[i][0];
+                ea += sm_g[i][1];
+                qa += sm_g[i][2];
+            }
+            p.sub[(size_t)b * p.nsub + task.c2] = SubSum{e, ea, qa, 1.0};
+        }
+        return;
+    }
     draw_chunk<DT, PT, VEC2, false>(p, b, task.c2, mask);
 }
 
@@ -2384,6 +2455,7 @@ struct Plan {
     int seqs_per_wg;   //   sequences per workgroup of the one launch
     long long grid_small;
     bool helpers;
+    bool fine;         //   one helper per sub-chunk (at most kFineHelpers of them), else one per draw chunk
     int status;
 };
 
@@ -2395,7 +2467,8 @@ Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, b
     q.nch1 = (vocab + chunk1 - 1) / chunk1;
     q.grid1 = (long long)(gamma + 1) * batch * q.nch1;
     q.helpers = !greedy && !tele;
-    q.gridh = q.helpers ? q.grid1 + (long long)batch * L.nch2 : q.grid1;
+    q.fine = q.helpers && (long long)batch * L.nsub <= kFineHelpers;
+    q.gridh = q.helpers ? q.grid1 + (long long)batch * (q.fine ? L.nsub : L.nch2) : q.grid1;
     q.grid2 = greedy || q.helpers ? (long long)batch : (long long)batch * L.nch2;
     q.gridb = tele ? (long long)batch * gamma * L.nchb : 0;
     q.small = vocab <= kSmallV && !tele;
@@ -2421,7 +2494,7 @@ Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, b
 // with an entry above the draft token's decides its position).
 constexpr int kMinRowWgsPerCu = 3, kMaxRowWgsPerCu = 8;
 constexpr int kSampleHalfPositions = 3, kGreedyHalfPositions = 4;
-constexpr int kStaticLdsMargin = 256;  // above the first launch's static LDS (< 100 bytes)
+constexpr int kStaticLdsMargin = 256;  // above the first launch's static LDS (< 200 bytes)
 
 inline int row_wgs_per_cu(long long blocks_per_position, int n_cu, int half_positions)
 {
@@ -2641,6 +2714,7 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
     p.nch1 = nch1;
     p.nch2 = L.nch2;
     p.nsub = L.nsub;
+    p.fine = q.fine ? 1 : 0;
     p.probs_dtype = probs_dtype;
     p.zero = 0u;
     p.c_hi = c_hi;

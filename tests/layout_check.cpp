@@ -124,7 +124,25 @@ static void check_shape(int B, int gamma, int V, int ldt, int pdt, bool greedy, 
         CHECK(q.grid2 == B, "greedy: one draw workgroup per sequence");
         return;
     }
-    if (q.helpers) {
+    if (q.helpers && q.fine) {
+        // one helper per sub-chunk, wave w on group w of it
+        CHECK((long long)B * L.nsub <= kFineHelpers, "fine helpers only for small batches");
+        CHECK(q.gridh == q.grid1 + (long long)B * L.nsub, "fine helpers follow the row blocks");
+        CHECK(q.grid2 == B, "last launch: one workgroup per sequence");
+        std::vector<int> seen((size_t)B * L.nsub, 0);
+        for (long long j = 0; j < (long long)B * L.nsub; ++j) {
+            const DrawTask t = fine_task((int)j, L.nsub);
+            CHECK(t.r >= 0 && t.r < B && t.c2 >= 0 && t.c2 < L.nsub, "fine helper %lld -> r=%d s=%d", j, t.r, t.c2);
+            if (t.r >= 0 && t.r < B && t.c2 >= 0 && t.c2 < L.nsub) ++seen[(size_t)t.r * L.nsub + t.c2];
+            for (int w = 0; w < kWaves; ++w) {
+                const long long grp = (long long)t.c2 * kSubPerWave + w;  // its first entry may lie past V (then no load)
+                CHECK(grp >= 0 && grp < (long long)L.nsub * kSubPerWave, "fine helper %lld wave %d -> group %lld", j, w, grp);
+            }
+            CHECK(sizeof(SubSum) * ((size_t)(B - 1) * L.nsub + t.c2 + 1) <= reg[6].need, "draw sums in their region");
+        }
+        for (size_t k = 0; k < seen.size(); ++k) CHECK(seen[k] == 1, "sub-chunk task %zu taken %d times", k, seen[k]);
+    } else if (q.helpers) {
+        CHECK((long long)B * L.nsub > kFineHelpers, "chunk helpers only for large batches");
         CHECK(q.gridh == q.grid1 + (long long)B * L.nch2, "helpers follow the row blocks");
         CHECK(q.grid2 == B, "last launch: one workgroup per sequence");
         for (long long j : probe((long long)B * L.nch2, L.nch2)) {
@@ -171,7 +189,7 @@ static void check_shape(int B, int gamma, int V, int ldt, int pdt, bool greedy, 
 
 // The first launch's occupancy cap: 3..8 row blocks per CU, growing with the
 // blocks of one position; the dynamic LDS lets exactly that many workgroups
-// share a CU (static LDS up to 100 bytes, allocation granules up to 1280).
+// share a CU (static LDS up to 200 bytes, allocation granules up to 1280).
 static void check_occupancy_cap()
 {
     for (int h : {kSampleHalfPositions, kGreedyHalfPositions})
@@ -197,7 +215,7 @@ static void check_occupancy_cap()
         CHECK(cap_lds_bytes(kMaxRowWgsPerCu, lds, lds) == 0u, "no cap at 8");
         for (int w = kMinRowWgsPerCu; w < kMaxRowWgsPerCu; ++w) {
             const long long d = cap_lds_bytes(w, lds, lds);
-            const long long held = (d + 100 + 1279) / 1280 * 1280;
+            const long long held = (d + 200 + 1279) / 1280 * 1280;
             CHECK(d > 0 && w * held <= lds && (w + 1) * d > lds, "lds=%d w=%d dyn=%lld", lds, w, d);
         }
         CHECK(cap_lds_bytes(3, lds, 1024) == 0u, "above the per-workgroup limit: no cap");
