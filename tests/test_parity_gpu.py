@@ -79,6 +79,16 @@ def test_c5_reduced(seed):
     _check(synth.make_inputs("c5", 300 + seed, B=8, V=70_000))
 
 
+@pytest.mark.parametrize("B", [64, 80, 100, 110])
+def test_capped_first_launch_depths(B):
+    """Batches of the c4 shape between c5's and c4's: the first launch's cap on
+    resident row blocks comes out at 4, 5, 6 and 7 workgroups per CU in sample
+    mode (5, 7, 8, 8 in greedy mode) on a 256-CU chip; outputs as everywhere."""
+    d = synth.make_inputs("c4", 3000 + B, B=B)
+    _check(d)
+    _check(d, mode="greedy", aux=False)
+
+
 @pytest.mark.parametrize("V", [1, 7, 8, 1001, 20_001])
 def test_unaligned_vocab_scalar_path(V):
     # V not a multiple of the vector width: scalar loads (bf16 and fp32)
