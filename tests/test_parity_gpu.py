@@ -174,6 +174,26 @@ def test_neg_inf_logits_and_zero_probs():
     _check(d)
 
 
+@pytest.mark.parametrize("T", [1.0, 0.05])
+def test_bf16_rows_with_extreme_negative_logits(T):
+    """bf16 rows holding -inf, the most negative finite bf16 and large
+    negative values beside ordinary logits, at two temperatures: every
+    exponential of those entries underflows to 0, in the row stage's fp32
+    and in the draw's fp64 alike."""
+    d = synth.make_inputs("c4", 804, B=24, V=40_000)
+    rng = np.random.default_rng(804)
+    zl = d["target_logits"]  # bf16 bit patterns
+    u = rng.random(zl.shape)
+    zl[u < 0.2] = 0xff80                                     # -inf
+    zl[(u >= 0.2) & (u < 0.25)] = 0xff7f                     # most negative finite
+    big = synth.f32_to_bf16_bits(-rng.uniform(100.0, 1e6, zl.shape).astype(np.float32))
+    sel = (u >= 0.25) & (u < 0.3)
+    zl[sel] = big[sel]
+    zl[:, :, :4] = synth.f32_to_bf16_bits(np.zeros((1,), np.float32))[0]  # every row's maximum finite
+    d["temperature"] = T
+    _check(d)
+
+
 def test_identical_distributions_take_bonus():
     B, gamma, V = 32, 5, 4096
     zl = np.zeros((B, gamma + 1, V), np.float32)
