@@ -2511,7 +2511,7 @@ inline unsigned cap_lds_bytes(int wgs, int lds_cu, int lds_block_max)
 {
     if (wgs >= kMaxRowWgsPerCu || wgs < 1 || lds_cu <= 0) return 0u;
     const long long dyn = 2LL * lds_cu / (2 * wgs + 1) - kStaticLdsMargin;
-    return dyn > 0 && dyn <= lds_block_max ? (unsigned)dyn : 0u;
+    return dyn > 0 && dyn + kStaticLdsMargin <= lds_block_max ? (unsigned)dyn : 0u;
 }
 
 // The checks of every verify entry point that need no workspace and no HIP

@@ -219,6 +219,10 @@ static void check_occupancy_cap()
             CHECK(d > 0 && w * held <= lds && (w + 1) * d > lds, "lds=%d w=%d dyn=%lld", lds, w, d);
         }
         CHECK(cap_lds_bytes(3, lds, 1024) == 0u, "above the per-workgroup limit: no cap");
+        for (int w = kMinRowWgsPerCu; w < kMaxRowWgsPerCu; ++w) {
+            const long long d = cap_lds_bytes(w, lds, 65536);
+            CHECK(d == 0 || d + 200 <= 65536, "dynamic and static LDS within a 64 KiB workgroup limit (w=%d)", w);
+        }
     }
 }
 
