@@ -106,6 +106,11 @@ constexpr int kSubPerPass = 2;  // first launch (the helpers share SIMDs with th
 // helpers' fixed costs (the ready-list poll, the row statistics) outweigh the
 // shorter draws.
 constexpr long long kFineHelpers = 1024;
+// Greedy calls on bf16 rows take kChunkFp32-entry row chunks when a position has
+// at most this many kChunkBf16-entry ones: with few rows the decisions, not the
+// streaming, set the pace, and shorter blocks reach them sooner (the cap on
+// resident row blocks then comes out at 8: none).
+constexpr long long kHalfChunkBlocks = 1024;
 constexpr int kSubPerChunk = kSubPerWave * kWaves;  // 16 groups in a draw chunk
 constexpr int kChunk2 = kSub * kSubPerChunk;        // 8192
 constexpr int kSubW = kSub * kSubPerWave;           // 2048 elements of a sub-chunk
@@ -1835,10 +1840,11 @@ __device__ __forceinline__ bool greedy_skipped(const Params& p, int b, int k, in
     return *sm_flag != 0;
 }
 
-template <int DT, bool VEC>
+// EPT: entries per thread (kEptBf16 or kEptFp32; for bf16 rows of small
+// batches kEptFp32, so half-size chunks, see make_plan).
+template <int DT, bool VEC, int EPT>
 __global__ __launch_bounds__(kThreads) void k_rows_greedy(const Params p)
 {
-    constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
     constexpr int W = DT == SV_BF16 ? 8 : 4;
     constexpr int CH = EPT * kThreads;
     const RowBlock rb = row_block(blockIdx.x, p.nch1, p.B);
@@ -2427,10 +2433,17 @@ bool launch_sample(int dt, int pt, int vmode, int grid1, unsigned lds1, int grid
 }
 
 template <int DT>
-bool launch_greedy_t(bool vec, int grid1, unsigned lds1, int B, const Params& p, hipStream_t s, hipEvent_t ev_mid)
+bool launch_greedy_t(bool vec, bool half_chunks, int grid1, unsigned lds1, int B, const Params& p, hipStream_t s,
+                     hipEvent_t ev_mid)
 {
-    if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true>), dim3(grid1), dim3(kThreads), lds1, s, p);
-    else hipLaunchKernelGGL((k_rows_greedy<DT, false>), dim3(grid1), dim3(kThreads), lds1, s, p);
+    constexpr int EPT = DT == SV_BF16 ? kEptBf16 : kEptFp32;
+    if (DT == SV_BF16 && half_chunks) {
+        if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true, kEptFp32>), dim3(grid1), dim3(kThreads), lds1, s, p);
+        else hipLaunchKernelGGL((k_rows_greedy<DT, false, kEptFp32>), dim3(grid1), dim3(kThreads), lds1, s, p);
+    } else {
+        if (vec) hipLaunchKernelGGL((k_rows_greedy<DT, true, EPT>), dim3(grid1), dim3(kThreads), lds1, s, p);
+        else hipLaunchKernelGGL((k_rows_greedy<DT, false, EPT>), dim3(grid1), dim3(kThreads), lds1, s, p);
+    }
     if (hipGetLastError() != hipSuccess) return false;
     if (ev_mid && hipEventRecord(ev_mid, s) != hipSuccess) return false;
     hipLaunchKernelGGL(k_draw_greedy, dim3(B), dim3(kThreads), 0, s, p);
@@ -2455,6 +2468,7 @@ struct Plan {
     int seqs_per_wg;   //   sequences per workgroup of the one launch
     long long grid_small;
     bool helpers;
+    bool half_chunks;  //   greedy, bf16 rows: kChunkFp32-entry row chunks (a small batch)
     bool fine;         //   one helper per sub-chunk (at most kFineHelpers of them), else one per draw chunk
     int status;
 };
@@ -2465,6 +2479,10 @@ Plan make_plan(int batch, int gamma, int vocab, int logits_dtype, bool greedy, b
     Plan q{};
     const int chunk1 = logits_dtype == SV_BF16 ? kChunkBf16 : kChunkFp32;
     q.nch1 = (vocab + chunk1 - 1) / chunk1;
+    // greedy calls on bf16 rows whose positions hold few row blocks take
+    // half-size chunks: shorter blocks move the decisions along sooner
+    q.half_chunks = greedy && logits_dtype == SV_BF16 && (long long)batch * q.nch1 <= kHalfChunkBlocks;
+    if (q.half_chunks) q.nch1 = (vocab + kChunkFp32 - 1) / kChunkFp32;
     q.grid1 = (long long)(gamma + 1) * batch * q.nch1;
     q.helpers = !greedy && !tele;
     q.fine = q.helpers && (long long)batch * L.nsub <= kFineHelpers;
@@ -2746,8 +2764,9 @@ int spec_verify_lenient(int batch, int gamma, int vocab,
             lds1 = cap_lds_bytes(row_wgs_per_cu((long long)batch * nch1, dp.n_cu, depth), dp.lds_cu, dp.lds_block);
         }
         if (greedy)
-            ok = logits_dtype == SV_BF16 ? launch_greedy_t<SV_BF16>(vec, (int)q.grid1, lds1, batch, p, s, ev_mid)
-                                         : launch_greedy_t<SV_FP32>(vec, (int)q.grid1, lds1, batch, p, s, ev_mid);
+            ok = logits_dtype == SV_BF16
+                     ? launch_greedy_t<SV_BF16>(vec, q.half_chunks, (int)q.grid1, lds1, batch, p, s, ev_mid)
+                     : launch_greedy_t<SV_FP32>(vec, false, (int)q.grid1, lds1, batch, p, s, ev_mid);
         else
             ok = launch_sample(logits_dtype, probs_dtype, vmode, (int)q.gridh, lds1, (int)q.grid2, p, s, ev_mid,
                                extras ? (hipEvent_t)extras->ev_tele : nullptr);

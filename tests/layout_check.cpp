@@ -104,7 +104,12 @@ static void check_shape(int B, int gamma, int V, int ldt, int pdt, bool greedy, 
 
     // the row stage (sample and greedy): every workgroup has a position,
     // sequence and chunk inside the problem, and its chunk starts inside the row
-    const int CH = ldt == SV_BF16 ? kChunkBf16 : kChunkFp32;
+    const int CH = ldt == SV_BF16 && !q.half_chunks ? kChunkBf16 : kChunkFp32;
+    CHECK(!q.half_chunks || (greedy && ldt == SV_BF16 &&
+                             (long long)B * ((V + kChunkBf16 - 1) / kChunkBf16) <= kHalfChunkBlocks),
+          "half-size chunks only for greedy bf16 calls of small batches");
+    CHECK((long long)q.nch1 * CH >= V && (long long)(q.nch1 - 1) * CH < V, "row chunks cover the row exactly");
+    CHECK(q.nch1 <= L.nch1_max, "row chunks within the partial region's sizing");
     for (long long bid : probe(q.grid1, q.nch1)) {
         const RowBlock rb = row_block((uint32_t)bid, q.nch1, B);
         CHECK(rb.k >= 0 && rb.k <= gamma && rb.b >= 0 && rb.b < B && rb.c >= 0 && rb.c < q.nch1,
