@@ -2288,18 +2288,18 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
             const int x = __shfl(tok, base + i, 64);
             const double ex = __shfl(ei, base + (x & (RL - 1)), 64);  // e_x: lane x of the row holds it (x < V <= RL)
             const float ui = __shfl(ul, base + i, 64);
-            double P = 0.0, Q = 0.0;
+            double Q = 0.0;
             bool rej = false;
             const float qi = __shfl(qx, base + i, 64);  // q_i(x_i)
             if (active) {
-                P = ex * (1.0 / Si);
                 Q = (double)qi;
-                // u <= min(1, p / (l q)), q <= 0 accepting, without the
-                // divisions: for u <= 1 the same as q <= 0 or u l q <= p
-                // (rounding can differ only within the flagged window)
-                rej = !((double)ui <= 1.0 && (Q <= 0.0 || (double)ui * (p.len * Q) <= P));
+                // u <= min(1, p / (l q)) with p = e_x / S_i, q <= 0 accepting,
+                // without divisions: for u <= 1 the same as q <= 0 or
+                // u l q S_i <= e_x (rounding can differ only within the
+                // flagged window)
+                rej = !((double)ui <= 1.0 && (Q <= 0.0 || (double)ui * (p.len * Q) * Si <= ex));
             }
-            if (active && l == i) { st_P = P; st_Q = Q; }
+            if (active && l == i) { st_P = ex; st_Q = Q; }  // (e_x here: p_i(x_i) = e_x / S_i at the output)
             if (active && rej) {
                 n = i;
                 active = false;
@@ -2347,7 +2347,7 @@ __global__ __launch_bounds__(kThreads) void k_tiny(const Params p)
         if (p.aux_rmax) p.aux_rmax[(int64_t)b * G1 + l] = row_seen ? st_m : NAN;
         if (p.aux_rsum) p.aux_rsum[(int64_t)b * G1 + l] = row_seen && !GREEDY ? st_S : NAN;
         if (l < p.gamma) {
-            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + l] = row_seen && !GREEDY ? st_P : NAN;
+            if (p.aux_p) p.aux_p[(int64_t)b * p.gamma + l] = row_seen && !GREEDY ? st_P / st_S : NAN;
             if (p.aux_q) p.aux_q[(int64_t)b * p.gamma + l] = row_seen && !GREEDY ? st_Q : NAN;
         }
     }
