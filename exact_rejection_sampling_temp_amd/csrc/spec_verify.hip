@@ -1678,19 +1678,25 @@ __global__ __launch_bounds__(kThreads) void k_beta(const Params p)
     const double mc = (double)__uint_as_float((uint32_t)ld_agent(sw)) * p.cd;
     const double S = __longlong_as_double((long long)ld_agent(sw + 1));
     const float K = (float)(-mc);
-    const double scale = exp2(-((double)K + mc)) / S;
+    // p_v = 2^(...) * scale in fp32 (the row stage's exponential, ~3e-7
+    // relative), min(p_v, q_v) in fp32, eight at a time into an fp64 sum:
+    // beta is reported to 1e-6 absolute
+    const float scale = (float)(exp2(-((double)K + mc)) / S);
+    const bool full = (c + 1) * kChunkB <= p.V;  // (uniform) no entry of the chunk past the row
 
     double acc = 0.0;
 #pragma unroll
     for (int g = 0; g < kGroupsB; ++g) {
         const int idx = c * kChunkB + (g * kThreads + tid) * 8;
+        float m8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float z = raw8_elem<DT>(zr[g], e);
-            const double pv = (double)__builtin_amdgcn_exp2f(fmaf(z, p.c_lo, fmaf(z, p.c_hi, K))) * scale;
-            const double m = fmin(pv, (double)raw8_elem<PT>(qr[g], e));
-            acc += idx + e < p.V ? m : 0.0;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(z, p.c_lo, fmaf(z, p.c_hi, K))) * scale;
+            m8[e] = fminf(pv, raw8_elem<PT>(qr[g], e));
+            if (!full && idx + e >= p.V) m8[e] = 0.0f;
         }
+        acc += (double)(((m8[0] + m8[1]) + (m8[2] + m8[3])) + ((m8[4] + m8[5]) + (m8[6] + m8[7])));
     }
     const double s = block_sum(acc, sm_d);
     if (tid == 0) p.bpart[(size_t)t * p.nchb + c] = s;
