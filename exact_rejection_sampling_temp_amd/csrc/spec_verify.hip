@@ -23,20 +23,25 @@
 //      finds an earlier position of its sequence rejected skips its chunk;
 //      with position-major launch order most unneeded rows are never read.
 //      The decider that completes a sequence's decisions appends it, with
-//      its n, to a ready list.  After every row workgroup the grid holds
-//      B * nch2 draw helpers: helper j waits (bounded) for the (j / nch2)-th
-//      sequence of the ready list and computes the fp64 sums of draw chunk
-//      j % nch2 of its row n (the residual max(0, p_n - q_n), or p_gamma
-//      when n = gamma), so the draws of the sequences resolved first overlap
-//      the rows of the others.
+//      its n, to a ready list.  After every row workgroup the grid holds the
+//      draw helpers: for each rank of the ready list one per draw chunk (one
+//      per sub-chunk in the smallest batches); a helper waits (bounded) for
+//      its rank's sequence and computes the fp64 sums of its part of row n
+//      (the residual max(0, p_n - q_n), or p_gamma when n = gamma), so the
+//      draws of the sequences resolved first overlap the rows of the others.
+//      For batches whose positions hold few row workgroups the launch takes
+//      dynamic LDS that caps its resident workgroups per CU, so that later
+//      positions do not stream rows ahead of the decisions that skip them.
 //
 //   2. k_finish_sample, one workgroup per sequence: it computes any draw
-//      chunk no helper did, turns the sums into the inverse-CDF draw, writes
-//      the outputs and clears the sequence's workspace.  (Calls that ask for
+//      chunk no helper did, turns the sums into the inverse-CDF draw (its
+//      four waves scanning the chosen sub-chunk's four groups side by side),
+//      writes the outputs and clears the sequence's workspace.  (Calls that ask for
 //      the acceptance telemetry stream every row and sweep the rows between
 //      the launches; their last launch is k_rest_sample.)
 //
-// Greedy mode is k_rows_greedy (same grid; chunk argmax) and k_draw_greedy.
+// Greedy mode is k_rows_greedy (same grid; chunk argmax; half-size chunks of
+// bf16 rows for small batches) and k_draw_greedy.
 //
 // Numerics.  The row stage uses fp32 exp2 with a two-term log2(e)/T and a
 // per-chunk correction of the rounded shift, and accumulates in fp64; the
