@@ -793,6 +793,9 @@ __device__ __forceinline__ bool row_arrive(const Params& p, int64_t row, int b, 
 {
     uint32_t last = 0;
     if (threadIdx.x == 0) {
+        // a chunk whose own evidence settles the rejection sets the bit at
+        // once, a round trip before the count's old value could
+        if (early_bit && evidence > kEvidenceThreshold) or_agent(&p.ctl[b].mask, early_bit);
         const uint64_t add = 1ull + (evidence << kCountBits) + dep;
         const uint64_t old = __hip_atomic_fetch_add(&p.cnt1[row], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = (old & kCountMask) + 1ull == (uint64_t)p.nch1 ? 1u : 0u;
